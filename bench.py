@@ -1,0 +1,288 @@
+"""Throughput of the vocab-parallel LM head + cross entropy on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch of the 8B-class
+shard workload (N = 8192 tokens, H = 4096, V = 128256, T = 8, shard 0 =
+[16032, 4096] bf16, Zipf(1.1) targets):
+
+    masked lookup of the batch's ids on shard 0          (vp_embed_fwd)
+    fused LM-head GEMM + statistics of shard 0           (vp_lmhead_ce_fwd)
+    merge of the 8 shards' statistics -> loss, lse, mean  (vp_ce_combine)
+    recompute, softmax - onehot, dX_0 and dW_0            (vp_lmhead_ce_bwd)
+
+The other seven shards' statistics are the other GPUs' work in a real
+deployment; they are computed once before timing.  Inputs are resident in HBM
+before the timed region.  Prints one JSON line (rank 0, N = 1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+PEAK_HBM_GBS = 8000.0
+METRIC = "tokens/sec fused LM-head+vocab-parallel CE fwd+bwd; % bf16 MFMA peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dev_bf16(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def cpu_baseline(inp, sample_tokens: int):
+    """The oracle, as it stands, timed on host cores for a bounded sample of tokens."""
+    import threadpoolctl
+
+    import oracle
+    import vp_inputs
+    cores = min(16, len(os.sched_getaffinity(0)))
+    wl = inp.wl
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(wl.N, sample_tokens, replace=False))
+    with threadpoolctl.threadpool_limits(limits=cores):
+        x = vp_inputs.bf16_bits_to_f64(inp.x[rows])
+        y = inp.targets[rows]
+        shards = [oracle.shard_range(wl.V, wl.T, t) for t in range(wl.T)]
+        w = [vp_inputs.bf16_bits_to_f64(inp.w[a:b]) for a, b in shards]
+        # other shards' statistics: inputs of the timed unit (other GPUs' work), untimed
+        others = [oracle.shard_stats(oracle.logits(x, w[t]), y, shards[t][0])
+                  for t in range(1, wl.T)]
+        g = oracle.mean_scale(inp.targets)
+        t0 = time.perf_counter()
+        z0 = oracle.logits(x, w[0])                                   # shard-0 forward
+        st0 = oracle.shard_stats(z0, y, 0)
+        stats = [st0] + others
+        loss, lse, mean = oracle.combine_triples(*(np.stack(a) for a in zip(*stats)), y)
+        dz0 = oracle.dz_rows(x, w[0], y, lse, 0, g)                   # shard-0 backward
+        dx0, dw0 = oracle.shard_grads(x, w[0], dz0)
+        dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample_tokens} of the {wl.N} tokens (seeded choice): shard-0 forward + "
+                      f"combine of 8 shards + shard-0 backward, NumPy fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--no-embed-bench", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(vocab shards would map one per GPU; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import vocab_lm_head_amd as vp
+    import vp_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    t0 = time.time()
+    inp = vp_inputs.make_inputs("shard_8b")
+    wl = inp.wl
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    N, H, V, T, Vs = wl.N, wl.H, wl.V, wl.T, wl.Vs
+    x_d = dev_bf16(torch, inp.x, dev)
+    w_full = dev_bf16(torch, inp.w, dev)
+    y_d = torch.from_numpy(inp.targets).to(dev)
+    ids_d = torch.from_numpy(inp.ids).to(dev)
+    ranges = [vp.vp_shard_range(V, T, t) for t in range(T)]
+    w0 = w_full[ranges[0][0]:ranges[0][1]]
+    n_valid = int((inp.targets != vp.DEFAULT_IGNORE_INDEX).sum())
+    grad_scale = 1.0 / max(1, n_valid)
+
+    # buffers and workspaces allocated once
+    m = torch.empty((T, N), dtype=torch.float32, device=dev)
+    s, zy = torch.empty_like(m), torch.empty_like(m)
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty_like(loss)
+    mean = torch.empty(1, dtype=torch.float32, device=dev)
+    emb = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((N, H), dtype=torch.float32, device=dev)
+    dw = torch.empty((Vs, H), dtype=torch.float32, device=dev)
+    ws_f = vp.alloc_workspace(vp.vp_lmhead_ce_fwd_workspace(N, H, 0, Vs), dev)
+    ws_b = vp.alloc_workspace(vp.vp_lmhead_ce_bwd_workspace(N, H, 0, Vs), dev)
+
+    # the other seven shards' statistics (untimed)
+    for t in range(1, T):
+        a, b = ranges[t]
+        vp.vp_lmhead_ce_fwd(x_d, w_full[a:b], y_d, a, b, m[t], s[t], zy[t], workspace=ws_f)
+
+    ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for k in ("embed", "fwd", "combine", "bwd")}
+
+    def step(record=None):
+        def mark(k, i):
+            if record is not None:
+                record[k][i].record(stream)
+        mark("embed", 0)
+        vp.vp_embed_fwd(ids_d, w0, 0, Vs, out=emb)
+        mark("embed", 1)
+        mark("fwd", 0)
+        vp.vp_lmhead_ce_fwd(x_d, w0, y_d, 0, Vs, m[0], s[0], zy[0], workspace=ws_f)
+        mark("fwd", 1)
+        mark("combine", 0)
+        vp.vp_ce_combine(m, s, zy, y_d, loss=loss, lse=lse, loss_mean=mean)
+        mark("combine", 1)
+        mark("bwd", 0)
+        vp.vp_lmhead_ce_bwd(x_d, w0, y_d, lse, 0, Vs, grad_scale, dx=dx, dw=dw, workspace=ws_b)
+        mark("bwd", 1)
+
+    # parity gate: no number is reported unless the loss matches the oracle
+    step()
+    torch.cuda.synchronize()
+    gold_path = os.path.join(ROOT, "tests", "golden", "oracle_shard_8b.npz")
+    parity = {"checked": False}
+    if os.path.exists(gold_path):
+        gold = np.load(gold_path)
+        lerr = float(np.abs(loss.cpu().double().numpy() - gold["loss"]).max())
+        parity = {"checked": True, "loss_max_abs_err": lerr, "bar": 2e-3,
+                  "mean_abs_err": abs(float(mean.item()) - float(gold["mean"]))}
+        if not lerr <= 2e-3:
+            log(f"PARITY FAILED: loss max abs err {lerr}")
+            print(json.dumps({"metric": METRIC, "value": None, "error": "parity failed",
+                              "parity": parity}))
+            sys.exit(1)
+    log(f"parity: {parity}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, bracketed by synchronisation
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # per-call durations with events on the same stream (separate pass, same work)
+    per = {k: [] for k in ev}
+    for _ in range(args.steps):
+        step(ev)
+        torch.cuda.synchronize()
+        for k, (a, b) in ev.items():
+            per[k].append(a.elapsed_time(b))
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    ce_ms = avg["fwd"] + avg["combine"] + avg["bwd"]
+    alg_flops = 6.0 * N * Vs * H
+    achieved = alg_flops / (ce_ms * 1e-3) / 1e12
+    exec_tflops = 8.0 * N * Vs * H / (ce_ms * 1e-3) / 1e12
+
+    embed_bytes = N * H * 2 + len(np.unique(inp.ids[inp.ids < Vs])) * H * 2 + N * 8
+    breakdown = {
+        "embed_ms": avg["embed"], "fwd_ms": avg["fwd"], "combine_ms": avg["combine"],
+        "bwd_ms": avg["bwd"],
+        "fwd_gemm_tflops": 2.0 * N * Vs * H / (avg["fwd"] * 1e-3) / 1e12,
+        "bwd_gemms_tflops_executed": 6.0 * N * Vs * H / (avg["bwd"] * 1e-3) / 1e12,
+        "ce_executed_tflops": exec_tflops,
+        "ce_executed_frac": exec_tflops / PEAK_BF16_TFLOPS,
+        "embed_GBs": embed_bytes / (avg["embed"] * 1e-3) / 1e9,
+    }
+
+    extra = {}
+    if not args.no_embed_bench:
+        extra["embedding_heavy_lookup"] = embed_bench(torch, vp, vp_inputs, dev, stream, args)
+
+    result = {
+        "metric": METRIC,
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "shard_8b: N=8192 tokens, H=4096, V=128256, T=8, shard 0 = "
+                               "[16032, 4096] bf16 (W~N(0,0.02), X~N(0,1)), Zipf(1.1) targets; "
+                               "step = lookup + fwd + combine(T=8) + bwd of shard 0",
+                   "global_batch": N, "hidden": H, "vocab": V, "shards": T,
+                   "parallelism": "1 GPU (one vocab shard)"},
+        "roofline": {"bound": "mfma", "kernel": "fused LM-head CE fwd+combine+bwd (vp_lmhead_ce_fwd + "
+                     "vp_ce_combine + vp_lmhead_ce_bwd)", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None, "algorithmic_flops_per_launch": alg_flops,
+                     "avg_launch_ms": ce_ms},
+        "breakdown": breakdown,
+        "parity": parity,
+        **extra,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample)
+    print(json.dumps(result))
+
+
+def embed_bench(torch, vp, vp_inputs, dev, stream, args):
+    """The embedding-heavy lookup: 65536 Zipf(1.0) ids on shard 0 ([64000, 4096] bf16) of
+    V = 256000, T = 4; algorithmic HBM bytes = output + distinct on-shard rows + ids."""
+    wl = vp_inputs.WORKLOADS["embedding_heavy"]
+    inp = vp_inputs.make_inputs("embedding_heavy", with_weight=False)
+    Vs_e = wl.embed_V // wl.embed_T
+    w_bits = vp_inputs.make_weight_rows(wl, 0, Vs_e)
+    w_d = dev_bf16(torch, w_bits, dev)
+    ids_d = torch.from_numpy(inp.ids).to(dev)
+    n, h = inp.ids.shape[0], wl.embed_H
+    out = torch.empty((n, h), dtype=torch.bfloat16, device=dev)
+    ids = inp.ids
+    own = ids[(ids >= 0) & (ids < Vs_e)]
+    distinct = len(np.unique(own))
+    alg_bytes = n * h * 2 + distinct * h * 2 + n * 8
+    # parity of this launch: bit-exact on a sample of rows
+    vp.vp_embed_fwd(ids_d, w_d, 0, Vs_e, out=out)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(5).choice(n, 512, replace=False)
+    got = out[torch.from_numpy(rows).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+    want = np.zeros((rows.size, h), dtype=np.uint16)
+    o = (ids[rows] >= 0) & (ids[rows] < Vs_e)
+    want[o] = w_bits[ids[rows][o]]
+    ok = bool(np.array_equal(got, want))
+    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+    times = []
+    for i in range(args.warmup + args.steps):
+        flush.fill_(float(i))          # evict L2 / MALL between repetitions
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        vp.vp_embed_fwd(ids_d, w_d, 0, Vs_e, out=out)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "median_ms": ms, "min_ms": float(np.min(times)),
+            "algorithmic_bytes": alg_bytes, "distinct_on_shard_rows": distinct,
+            "on_shard_ids": int(own.size), "bit_exact_sample": ok}
+
+
+if __name__ == "__main__":
+    main()

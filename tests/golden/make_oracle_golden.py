@@ -1,0 +1,88 @@
+"""Write the oracle's expected values for the full-size workloads.
+
+    python tests/golden/make_oracle_golden.py [workload ...]
+
+Calls only ``oracle/`` (fp64 NumPy) and the seeded input generators
+(``vp_inputs``); nothing from the HIP path.  For each workload whose dense
+logits are too large to recompute inside a GPU test, it stores per token
+
+  lse   the full-vocabulary log-sum-exp (fp64)
+  loss  the per-token cross entropy (fp64)
+
+in ``oracle_<workload>.npz`` next to this script.  The GPU tests regenerate
+the same input bits from the same seeds and derive everything else they
+compare (statistics of shard 0, sampled rows of dX and dW) from these values
+with the oracle at test time.
+"""
+from __future__ import annotations
+
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import vp_inputs  # noqa: E402
+
+
+def _f64(bits):
+    return vp_inputs.bf16_bits_to_f64(bits)
+
+
+def _dense_chunked(x, w, targets, chunk):
+    """oracle.dense_ce over the full vocabulary, one chunk of tokens at a time."""
+    n = x.shape[0]
+    lse, loss = np.empty(n), np.empty(n)
+    for a in range(0, n, chunk):
+        loss[a:a + chunk], lse[a:a + chunk], _ = oracle.dense_ce(
+            oracle.logits(x[a:a + chunk], w), targets[a:a + chunk])
+    valid = targets != oracle.DEFAULT_IGNORE_INDEX
+    return {"lse": lse, "loss": loss, "mean": np.array(loss[valid].sum() / max(1, int(valid.sum())))}
+
+
+def golden_shard_8b():
+    """Dense cross entropy over all V = 128256 rows (all eight shards materialised)."""
+    inp = vp_inputs.make_inputs("shard_8b")
+    return _dense_chunked(_f64(inp.x), _f64(inp.w), inp.targets, chunk=512)
+
+
+def golden_large_vocab():
+    """Shard 0 computed from data, shards 1..7 from the synthetic statistics."""
+    inp = vp_inputs.make_inputs("large_vocab")
+    m, s, zy = vp_inputs.synthetic_triples("large_vocab", inp.targets)
+    m0, s0, zy0 = oracle.shard_stats_chunked(_f64(inp.x), _f64(inp.w), inp.targets, 0, chunk=512)
+    M = m.astype(np.float64)
+    S = s.astype(np.float64)
+    Z = zy.astype(np.float64)
+    M[0], S[0], Z[0] = m0, s0, zy0
+    loss, lse, mean = oracle.combine_triples(M, S, Z, inp.targets)
+    return {"lse": lse, "loss": loss, "mean": np.array(mean)}
+
+
+def golden_embedding_heavy():
+    """T = 1 cross entropy over the full V = 256000 on N = 4096 tokens."""
+    inp = vp_inputs.make_inputs("embedding_heavy")
+    return _dense_chunked(_f64(inp.x), _f64(inp.w), inp.targets, chunk=256)
+
+
+MAKERS = {"shard_8b": golden_shard_8b, "large_vocab": golden_large_vocab,
+          "embedding_heavy": golden_embedding_heavy}
+
+
+def main(names):
+    for name in names or list(MAKERS):
+        t = time.time()
+        out = MAKERS[name]()
+        path = os.path.join(HERE, f"oracle_{name}.npz")
+        np.savez_compressed(path, **out)
+        print(f"{name}: wrote {path} in {time.time() - t:.1f}s  mean loss {float(out['mean']):.6f}",
+              flush=True)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

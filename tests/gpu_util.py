@@ -1,0 +1,96 @@
+"""Helpers of the GPU parity tests: moving input bits to the device, running the
+HIP path through the C ABI binding, and the comparison bars.
+
+Tolerances (floating point; see the design doc for their derivation):
+  per-token loss and lse     max abs error <= 2e-3
+  dX, dW                     max|gpu - oracle| / max|oracle| <= 1e-2 per tensor
+  shard statistics m, zy     max abs error <= 2e-3;  s: max relative error <= 2e-3
+Integer / byte work (the embedding) is compared bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+LOSS_ATOL = 2e-3
+GRAD_RTOL = 1e-2
+STAT_ATOL = 2e-3
+STAT_RTOL = 2e-3
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def dev_i64(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int64)).to(device)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def rel_max(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.abs(b).max()
+    num = np.abs(a - b).max()
+    return float(num / den) if den > 0 else float(num)
+
+
+def assert_loss_close(gpu, ref, what="loss"):
+    err = float(np.abs(np.asarray(gpu, np.float64) - np.asarray(ref, np.float64)).max())
+    log(f"  {what}: max abs err {err:.3e} (bar {LOSS_ATOL})")
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
+    assert err <= LOSS_ATOL, f"{what}: max abs err {err} > {LOSS_ATOL}"
+
+
+def assert_grad_close(gpu, ref, what):
+    e = rel_max(gpu, ref)
+    log(f"  {what}: max|d|/max|ref| {e:.3e} (bar {GRAD_RTOL})")
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
+    assert e <= GRAD_RTOL, f"{what}: relative error {e} > {GRAD_RTOL}"
+
+
+def assert_stats_close(gpu, ref, what="stats"):
+    (gm, gs, gz), (rm, rs, rz) = gpu, ref
+    em = float(np.abs(gm - rm).max())
+    ez = float(np.abs(gz - rz).max())
+    es = float((np.abs(gs - rs) / np.abs(rs)).max())
+    log(f"  {what}: m {em:.2e}  s(rel) {es:.2e}  zy {ez:.2e}")
+    assert em <= STAT_ATOL and ez <= STAT_ATOL and es <= STAT_RTOL, (em, es, ez)
+
+
+def run_ce_path(vp, x_d, w_shards_d, starts, ends, tgt_d, grad_scale, bwd_shards,
+                ignore_index=-100, stats_rows=None):
+    """All shards' forwards -> combine -> selected shards' backwards, on the GPU.
+
+    Returns dict with loss, lse, mean (device tensors), the stacked statistics
+    [T, n], and {shard: (dx, dw)} for ``bwd_shards``.
+    """
+    n = x_d.shape[0]
+    T = len(w_shards_d)
+    m = torch.empty((T, n), dtype=torch.float32, device=x_d.device)
+    s = torch.empty_like(m)
+    zy = torch.empty_like(m)
+    for t in range(T):
+        if stats_rows is not None and t in stats_rows:
+            m[t], s[t], zy[t] = stats_rows[t]
+            continue
+        vp.vp_lmhead_ce_fwd(x_d, w_shards_d[t], tgt_d, starts[t], ends[t], m[t], s[t], zy[t])
+    loss, lse, mean = vp.vp_ce_combine(m, s, zy, tgt_d, ignore_index)
+    grads = {}
+    for t in bwd_shards:
+        grads[t] = vp.vp_lmhead_ce_bwd(x_d, w_shards_d[t], tgt_d, lse, starts[t], ends[t],
+                                       grad_scale, ignore_index)
+    torch.cuda.synchronize()
+    return {"loss": loss, "lse": lse, "mean": mean, "m": m, "s": s, "zy": zy, "grads": grads}

@@ -1,0 +1,166 @@
+"""The C ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before launching anything.
+
+Only calls that fail validation (or are pure host functions) are made here;
+fake device addresses are never dereferenced because validation returns first.
+"""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "vocab_lm_head_amd", "libvplmhead.so")
+
+OK, NULL, SHAPE, RANGE, ALIGN, WORKSPACE, HIP = 0, -1, -2, -3, -4, -5, -6
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w \*]*?\b(vp_\w+)\s*\(", src, flags=re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built (python -m vocab_lm_head_amd.build)")
+    from vocab_lm_head_amd import _lib
+    return _lib.lib
+
+
+def test_header_declares_the_four_entry_points():
+    d = _declared()
+    for name in ("vp_embed_fwd", "vp_lmhead_ce_fwd", "vp_ce_combine", "vp_lmhead_ce_bwd"):
+        assert name in d
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (vp_\w+)$", out, flags=re.M))
+    declared = _declared()
+    assert declared, "no declarations parsed from include/*.h"
+    assert declared <= exported, f"missing exports: {declared - exported}"
+    from vocab_lm_head_amd import _lib
+    assert set(_lib.SIGNATURES) == declared, "binding signatures must cover exactly the header"
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, SHAPE, RANGE, ALIGN, WORKSPACE, HIP):
+        assert lib.vp_status_string(code)
+    assert b"unknown" in lib.vp_status_string(12345)
+
+
+def test_shard_range(lib):
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.vp_shard_range(128256, 8, 3, ctypes.byref(a), ctypes.byref(b)) == OK
+    assert (a.value, b.value) == (3 * 16032, 4 * 16032)
+    assert lib.vp_shard_range(152064, 8, 7, ctypes.byref(a), ctypes.byref(b)) == OK
+    assert (a.value, b.value) == (7 * 19008, 152064)
+    assert lib.vp_shard_range(10, 4, 0, ctypes.byref(a), ctypes.byref(b)) == SHAPE   # V % T
+    assert lib.vp_shard_range(8, 0, 0, ctypes.byref(a), ctypes.byref(b)) == SHAPE
+    assert lib.vp_shard_range(8, 2, 2, ctypes.byref(a), ctypes.byref(b)) == RANGE
+    assert lib.vp_shard_range(8, 2, -1, ctypes.byref(a), ctypes.byref(b)) == RANGE
+    assert lib.vp_shard_range(8, 2, 0, None, ctypes.byref(b)) == NULL
+
+
+FAKE = 0x10000          # 256-byte aligned, never dereferenced (validation fails first)
+FAKE_ODD = 0x10002
+
+
+def test_embed_validation(lib):
+    f = lib.vp_embed_fwd
+    assert f(FAKE, -1, FAKE, 0, 8, 16, FAKE, None) == SHAPE
+    assert f(FAKE, 4, FAKE, 0, 8, 0, FAKE, None) == SHAPE
+    assert f(FAKE, 4, FAKE, 8, 8, 16, FAKE, None) == RANGE
+    assert f(FAKE, 4, FAKE, -1, 8, 16, FAKE, None) == RANGE
+    assert f(FAKE, 4, FAKE, 0, 8, 12, FAKE, None) == ALIGN
+    assert f(None, 4, FAKE, 0, 8, 16, FAKE, None) == NULL
+    assert f(FAKE, 4, None, 0, 8, 16, FAKE, None) == NULL
+    assert f(FAKE, 4, FAKE, 0, 8, 16, None, None) == NULL
+    assert f(FAKE, 4, FAKE_ODD, 0, 8, 16, FAKE, None) == ALIGN
+    assert f(FAKE + 4, 4, FAKE, 0, 8, 16, FAKE, None) == ALIGN
+    assert f(None, 0, None, 0, 8, 16, None, None) == OK      # n == 0: nothing to do
+
+
+def test_fwd_validation_and_workspace(lib):
+    ws = lib.vp_lmhead_ce_fwd_workspace
+    assert ws(0, 4096, 0, 16032) == 0
+    need = ws(8192, 4096, 0, 16032)
+    slices = -(-16032 // 128)
+    assert need == -(-(3 * slices * 8192 * 4) // 256) * 256
+    assert ws(8192, 12, 0, 16032) == 0          # invalid h -> 0
+    f = lib.vp_lmhead_ce_fwd
+    args = lambda **k: [k.get("x", FAKE), k.get("w", FAKE), k.get("t", FAKE), k.get("n", 8192),
+                        k.get("h", 4096), k.get("lo", 0), k.get("hi", 16032), FAKE, FAKE, FAKE,
+                        k.get("ws", FAKE), k.get("wsb", need), None]
+    assert f(*args(ws=None)) == WORKSPACE
+    assert f(*args(wsb=need - 1)) == WORKSPACE
+    assert f(*args(ws=FAKE + 16)) == WORKSPACE                # not 256-byte aligned
+    assert f(*args(x=None)) == NULL
+    assert f(*args(t=FAKE + 4)) == ALIGN
+    assert f(*args(w=FAKE_ODD)) == ALIGN
+    assert f(*args(h=4100)) == ALIGN
+    assert f(*args(n=-5)) == SHAPE
+    assert f(*args(hi=0)) == RANGE
+    assert f(*args(n=0, x=None, w=None, t=None, ws=None, wsb=0)) == OK
+
+
+def test_combine_validation(lib):
+    f = lib.vp_ce_combine
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 0, -100, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, -1, 2, -100, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, 16, 2, -100, FAKE, FAKE, None, None) == NULL
+    assert f(None, FAKE, FAKE, FAKE, 16, 2, -100, FAKE, FAKE, FAKE, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE + 4, 16, 2, -100, FAKE, FAKE, FAKE, None) == ALIGN
+
+
+def test_bwd_validation_and_workspace(lib):
+    ws = lib.vp_lmhead_ce_bwd_workspace
+    n, h, vs = 8192, 4096, 16032
+    need = ws(n, h, 0, vs)
+    r256 = lambda b: -(-b // 256) * 256
+    assert need == r256(h * n * 2) + r256(h * vs * 2) + r256(n * vs * 2) + r256(vs * n * 2)
+    assert ws(6, 32, 0, 4) == r256(32 * 8 * 2) * 2 + r256(6 * 8 * 2) + r256(4 * 8 * 2)
+    f = lib.vp_lmhead_ce_bwd
+    base = dict(x=FAKE, w=FAKE, t=FAKE, lse=FAKE, n=n, h=h, lo=0, hi=vs, ign=-100, g=1.0,
+                dx=FAKE, dw=FAKE, ws=FAKE, wsb=need)
+    call = lambda **k: f(*[{**base, **k}[a] for a in ("x", "w", "t", "lse", "n", "h", "lo", "hi",
+                                                      "ign", "g", "dx", "dw", "ws", "wsb")], None)
+    assert call(dw=None) == NULL
+    assert call(lse=None) == NULL
+    assert call(wsb=need - 256) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(dx=FAKE + 8) == ALIGN
+    assert call(h=8, hi=0) == RANGE
+    assert call(n=-1) == SHAPE
+
+
+def test_product_package_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The binding must raise (not fall back) when the shared library is absent."""
+    import importlib.util
+    src = os.path.join(ROOT, "vocab_lm_head_amd", "_lib.py")
+    dst = tmp_path / "_lib.py"
+    dst.write_text(open(src).read())   # a copy with no libvplmhead.so beside it
+    spec = importlib.util.spec_from_file_location("vp_lib_copy", dst)
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="no CPU fallback"):
+        spec.loader.exec_module(mod)
+
+
+def test_product_does_not_reference_oracle():
+    """Nothing under the package imports or names the oracle."""
+    pkg = os.path.join(ROOT, "vocab_lm_head_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if os.path.isfile(path) and path.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+            txt = open(path).read()
+            assert not re.search(r"\boracle\b", txt), path

@@ -1,0 +1,208 @@
+"""Edge cases of the HIP path against the oracle: ragged tiles, ignore_index,
+degenerate shards, closed forms, empty inputs and lookup boundaries.  All go
+through the C ABI binding."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import vp_inputs
+from gpu_util import (assert_grad_close, assert_loss_close, assert_stats_close, bf16_bits,
+                      dev_bf16, dev_i64, host, log, run_ce_path)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vp():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vocab_lm_head_amd
+    return vocab_lm_head_amd
+
+
+def _problem(seed, N, H, V, x_std=1.0, logit_std=3.0, ignore_frac=0.0):
+    r = np.random.default_rng(seed)
+    xb = vp_inputs.f32_to_bf16_bits(r.standard_normal((N, H)).astype(np.float32) * x_std)
+    wb = vp_inputs.f32_to_bf16_bits(
+        r.standard_normal((V, H)).astype(np.float32) * (logit_std / math.sqrt(H) / x_std))
+    y = r.integers(0, V, N).astype(np.int64)
+    if ignore_frac:
+        y[r.random(N) < ignore_frac] = -100
+    return xb, wb, y
+
+
+def _full_check(vp, xb, wb, y, T, bwd_shards=None, label=""):
+    N, H = xb.shape
+    V = wb.shape[0]
+    x, w = vp_inputs.bf16_bits_to_f64(xb), vp_inputs.bf16_bits_to_f64(wb)
+    z = oracle.logits(x, w)
+    loss, lse, mean = oracle.dense_ce(z, y)
+    dz = oracle.dense_dlogits(z, y)
+    g = oracle.mean_scale(y)
+    rng = [oracle.shard_range(V, T, t) for t in range(T)]
+    x_d, w_d, y_d = dev_bf16(xb), dev_bf16(wb), dev_i64(y)
+    bwd = list(range(T)) if bwd_shards is None else bwd_shards
+    log(f"  case {label}: N={N} H={H} V={V} T={T}")
+    out = run_ce_path(vp, x_d, [w_d[a:b] for a, b in rng], [a for a, _ in rng],
+                      [b for _, b in rng], y_d, g, bwd_shards=bwd)
+    for t, (a, b) in enumerate(rng):
+        assert_stats_close((host(out["m"][t]), host(out["s"][t]), host(out["zy"][t])),
+                           oracle.shard_stats(z[:, a:b], y, a), f"shard {t} stats")
+    assert_loss_close(host(out["loss"]), loss)
+    assert_loss_close(host(out["lse"]), lse, "lse")
+    assert abs(float(out["mean"].item()) - mean) <= 2e-3
+    for t in bwd:
+        a, b = rng[t]
+        dxr, dwr = oracle.shard_grads(x, w[a:b], dz[:, a:b])
+        assert_grad_close(host(out["grads"][t][0]), dxr, f"dX partial {t}")
+        assert_grad_close(host(out["grads"][t][1]), dwr, f"dW {t}")
+    return out
+
+
+def test_ragged_tiles(vp):
+    """N, Vs and H all off the 256 / 64 tile grid: 300 tokens, 3 shards of 700, H = 136."""
+    xb, wb, y = _problem(1, 300, 136, 2100)
+    _full_check(vp, xb, wb, y, T=3, label="ragged")
+
+
+def test_ignore_index(vp):
+    xb, wb, y = _problem(2, 257, 64, 1024, ignore_frac=0.3)
+    out = _full_check(vp, xb, wb, y, T=2, label="ignore_index 30%")
+    ign = y == -100
+    assert not host(out["loss"])[ign].any()
+    for t in out["grads"]:
+        assert not host(out["grads"][t][0])[ign].any(), "ignored tokens must get dX = 0"
+
+
+def test_all_ignored(vp):
+    """N_valid = 0: mean 0 (max(1, N_valid) guard), loss 0, every gradient 0."""
+    xb, wb, y = _problem(3, 40, 32, 96)
+    y[:] = -100
+    out = _full_check(vp, xb, wb, y, T=2, label="all ignored")
+    assert float(out["mean"].item()) == 0.0
+    for t in out["grads"]:
+        assert not host(out["grads"][t][0]).any() and not host(out["grads"][t][1]).any()
+
+
+def test_degenerate_one_row_shards(vp):
+    """Vs = 1 (V = T = 4), one token, H = 8 (a single partial K step)."""
+    xb, wb, y = _problem(4, 1, 8, 4)
+    _full_check(vp, xb, wb, y, T=4, label="Vs=1")
+    xb, wb, y = _problem(5, 3, 8, 4)
+    _full_check(vp, xb, wb, y, T=1, label="T=1, V=4")
+
+
+def test_targets_on_shard_edges(vp):
+    N, H, V, T = 64, 96, 512, 4
+    xb, wb, _ = _problem(6, N, H, V)
+    Vs = V // T
+    edges = np.array([t * Vs + d for t in range(T) for d in (0, Vs - 1)], dtype=np.int64)
+    y = np.resize(edges, N)
+    _full_check(vp, xb, wb, y, T=T, label="edge targets")
+
+
+def test_large_logits(vp):
+    """Logit std 40: the stabilising maximum matters; sum-exp must not overflow."""
+    xb, wb, y = _problem(7, 130, 128, 640, logit_std=40.0)
+    _full_check(vp, xb, wb, y, T=2, label="logit std 40")
+
+
+def test_uniform_logits_closed_form(vp):
+    """W = 0 -> every logit equal -> loss = log V exactly, at the 8B-class shard shape."""
+    import json
+    import os
+    import torch
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "ce_closed_forms.json")))
+    V = 128256
+    want = [c["loss"] for c in gold["uniform"]["cases"] if c["V"] == V][0]
+    N, H, T = 512, 4096, 8
+    r = np.random.default_rng(8)
+    x_d = dev_bf16(vp_inputs.f32_to_bf16_bits(r.standard_normal((N, H)).astype(np.float32)))
+    w_d = torch.zeros((V // T, H), dtype=torch.bfloat16, device="cuda")
+    y = r.integers(0, V, N).astype(np.int64)
+    y_d = dev_i64(y)
+    rng = [oracle.shard_range(V, T, t) for t in range(T)]
+    out = run_ce_path(vp, x_d, [w_d] * T, [a for a, _ in rng], [b for _, b in rng], y_d,
+                      1.0 / N, bwd_shards=[0])
+    loss = host(out["loss"])
+    log(f"  uniform: loss range [{loss.min():.7f}, {loss.max():.7f}] vs log V = {want:.7f}")
+    assert np.abs(loss - want).max() <= 2e-3
+    # gradient closed form: dz = (1/V - [j == y]) / N, so dW_0[j] = (X^T (1/V - onehot_j)) / N
+    x = vp_inputs.bf16_bits_to_f64(bf16_bits(x_d))
+    Vs = V // T
+    onehot = (y[:, None] == np.arange(Vs)[None, :]).astype(np.float64)
+    dz0 = (1.0 / V - onehot) / N
+    assert_grad_close(host(out["grads"][0][1]), dz0.T @ x, "dW_0 closed form")
+    assert not host(out["grads"][0][0]).any(), "dX_0 = dz_0 W_0 = 0 when W_0 = 0"
+
+
+def test_empty_inputs(vp):
+    import torch
+    d = "cuda"
+    x = torch.empty((0, 16), dtype=torch.bfloat16, device=d)
+    w = torch.zeros((8, 16), dtype=torch.bfloat16, device=d)
+    y = torch.empty(0, dtype=torch.int64, device=d)
+    out = vp.vp_embed_fwd(y, w, 0, 8)
+    assert out.shape == (0, 16)
+    m, s, zy = vp.vp_lmhead_ce_fwd(x, w, y, 0, 8)
+    assert m.shape == (0,)
+    st = torch.empty((2, 0), dtype=torch.float32, device=d)
+    loss, lse, mean = vp.vp_ce_combine(st, st, st, y)
+    lse_in = torch.empty(0, dtype=torch.float32, device=d)
+    dw = torch.full((8, 16), 7.0, dtype=torch.float32, device=d)
+    dx, dw = vp.vp_lmhead_ce_bwd(x, w, y, lse_in, 0, 8, 1.0, dw=dw)
+    torch.cuda.synchronize()
+    assert float(mean.item()) == 0.0
+    assert not dw.any().item(), "no tokens -> dW = 0"
+
+
+def test_embedding_boundaries(vp):
+    V, T, H = 4096, 4, 8
+    r = np.random.default_rng(9)
+    wb = r.integers(0, 65536, (V, H)).astype(np.uint16)
+    Vs = V // T
+    ids = np.concatenate([[-1, -100, V, V + 5, 2**40, -(2**40)],
+                          [t * Vs + d for t in range(T) for d in (-1, 0, 1, Vs - 1)],
+                          r.integers(-10, V + 10, 1000)]).astype(np.int64)
+    w_d, ids_d = dev_bf16(wb), dev_i64(ids)
+    total = np.zeros((ids.size, H), dtype=np.uint64)
+    for t in range(T):
+        lo, hi = oracle.shard_range(V, T, t)
+        got = bf16_bits(vp.vp_embed_fwd(ids_d, w_d[lo:hi], lo, hi))
+        want = oracle.embed_shard(ids, wb[lo:hi], lo, hi)
+        assert np.array_equal(got, want), f"shard {t}"
+        total += got
+    inr = (ids >= 0) & (ids < V)
+    assert np.array_equal(total[inr].astype(np.uint16), wb[ids[inr]])
+    assert not total[~inr].any()
+
+
+def test_embedding_wide_rows(vp):
+    """H = 8200 (not a multiple of the 4 x 64 x 8 unrolled row step), odd N."""
+    V, T, H = 300, 3, 8200
+    r = np.random.default_rng(10)
+    wb = r.integers(0, 65536, (V, H)).astype(np.uint16)
+    ids = r.integers(-3, V + 3, 777).astype(np.int64)
+    w_d, ids_d = dev_bf16(wb), dev_i64(ids)
+    for t in range(T):
+        lo, hi = oracle.shard_range(V, T, t)
+        got = bf16_bits(vp.vp_embed_fwd(ids_d, w_d[lo:hi], lo, hi))
+        assert np.array_equal(got, oracle.embed_shard(ids, wb[lo:hi], lo, hi))
+
+
+def test_invalid_arguments_raise(vp):
+    import torch
+    d = "cuda"
+    x = torch.zeros((4, 12), dtype=torch.bfloat16, device=d)   # H % 8 != 0
+    w = torch.zeros((8, 12), dtype=torch.bfloat16, device=d)
+    y = torch.zeros(4, dtype=torch.int64, device=d)
+    with pytest.raises(vp.VPError) as e:
+        vp.vp_lmhead_ce_fwd(x, w, y, 0, 8)
+    assert e.value.status == -4
+    with pytest.raises(vp.VPError):
+        vp.vp_shard_range(10, 4, 0)

@@ -1,0 +1,12 @@
+"""MI355X-native vocab-parallel LM head + cross entropy.
+
+The work happens in ``libvplmhead.so`` (hand-written HIP for gfx950, C ABI in
+``include/vp_lmhead.h``); this package only builds it (``build``) and binds it
+(``_lib``).  Importing the package needs the built library -- there is no CPU
+fallback.
+"""
+from ._lib import (  # noqa: F401
+    DEFAULT_IGNORE_INDEX, VPError, alloc_workspace, lib, status_string, vp_ce_combine,
+    vp_embed_fwd, vp_lmhead_ce_bwd, vp_lmhead_ce_bwd_workspace, vp_lmhead_ce_fwd,
+    vp_lmhead_ce_fwd_workspace, vp_shard_range,
+)

@@ -1,0 +1,204 @@
+"""ctypes binding of ``libvplmhead.so`` -- argument marshalling only.
+
+Each function takes torch tensors that already live on the GPU, checks dtypes
+and shapes, passes ``data_ptr()`` values and the current HIP stream to the C
+entry point of the same name, and raises ``VPError`` on a non-zero status.
+Every step of the computation runs in the library's HIP kernels; nothing here
+computes a result.  If the library has not been built, importing this module
+fails loudly -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvplmhead.so")
+
+VP_OK = 0
+DEFAULT_IGNORE_INDEX = -100
+
+# symbol -> (restype, argtypes); the names and order follow include/vp_lmhead.h
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "vp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "vp_shard_range": (ctypes.c_int, [_I64, _I32, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "vp_embed_fwd": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _P]),
+    "vp_lmhead_ce_fwd_workspace": (_SZ, [_I64, _I64, _I64, _I64]),
+    "vp_lmhead_ce_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "vp_ce_combine": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I64, _P, _P, _P, _P]),
+    "vp_lmhead_ce_bwd_workspace": (_SZ, [_I64, _I64, _I64, _I64]),
+    "vp_lmhead_ce_bwd": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                        ctypes.c_float, _P, _P, _P, _SZ, _P]),
+}
+
+
+class VPError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first with `python -m vocab_lm_head_amd.build` "
+            "(the HIP library is required; there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.vp_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != VP_OK:
+        raise VPError(status, where)
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, dtype, ndim, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+def vp_shard_range(V: int, T: int, t: int):
+    a, b = _I64(), _I64()
+    _check(lib.vp_shard_range(int(V), int(T), int(t), ctypes.byref(a), ctypes.byref(b)),
+           "vp_shard_range")
+    return a.value, b.value
+
+
+def vp_embed_fwd(ids, w_shard, vocab_start: int, vocab_end: int, out=None, stream=None):
+    """Masked lookup of one shard: out[i] = w_shard[ids[i]-start] if owned, else 0."""
+    _need(ids, torch.int64, 1, "ids")
+    _need(w_shard, torch.bfloat16, 2, "w_shard")
+    n, h = ids.shape[0], w_shard.shape[1]
+    if w_shard.shape[0] != vocab_end - vocab_start:
+        raise ValueError("w_shard rows must equal vocab_end - vocab_start")
+    if out is None:
+        out = torch.empty((n, h), dtype=torch.bfloat16, device=w_shard.device)
+    _need(out, torch.bfloat16, 2, "out")
+    if tuple(out.shape) != (n, h):
+        raise ValueError("out must be [n, h]")
+    _check(lib.vp_embed_fwd(_ptr(ids), n, _ptr(w_shard), int(vocab_start), int(vocab_end), h,
+                            _ptr(out), _stream(stream)), "vp_embed_fwd")
+    return out
+
+
+def vp_lmhead_ce_fwd_workspace(n: int, h: int, vocab_start: int, vocab_end: int) -> int:
+    return int(lib.vp_lmhead_ce_fwd_workspace(n, h, vocab_start, vocab_end))
+
+
+def vp_lmhead_ce_bwd_workspace(n: int, h: int, vocab_start: int, vocab_end: int) -> int:
+    return int(lib.vp_lmhead_ce_bwd_workspace(n, h, vocab_start, vocab_end))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A byte tensor for a workspace (torch's allocator returns 256-byte aligned blocks)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def vp_lmhead_ce_fwd(hidden, w_shard, targets, vocab_start: int, vocab_end: int,
+                     m_local=None, s_local=None, zy_local=None, workspace=None, stream=None):
+    """Per-token (local max, local sum-exp, owned target logit) of one shard, fp32 [n] each."""
+    _need(hidden, torch.bfloat16, 2, "hidden")
+    _need(w_shard, torch.bfloat16, 2, "w_shard")
+    _need(targets, torch.int64, 1, "targets")
+    n, h = hidden.shape
+    if w_shard.shape != (vocab_end - vocab_start, h) or targets.shape[0] != n:
+        raise ValueError("shape mismatch between hidden, w_shard, targets and the vocab range")
+    dev = hidden.device
+    outs = []
+    for t in (m_local, s_local, zy_local):
+        if t is None:
+            t = torch.empty(n, dtype=torch.float32, device=dev)
+        _need(t, torch.float32, 1, "statistics output")
+        if t.shape[0] != n:
+            raise ValueError("statistics outputs must have n elements")
+        outs.append(t)
+    need = vp_lmhead_ce_fwd_workspace(n, h, vocab_start, vocab_end)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib.vp_lmhead_ce_fwd(_ptr(hidden), _ptr(w_shard), _ptr(targets), n, h, int(vocab_start),
+                                int(vocab_end), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream)), "vp_lmhead_ce_fwd")
+    return tuple(outs)
+
+
+def vp_ce_combine(m, s, zy, targets, ignore_index: int = DEFAULT_IGNORE_INDEX,
+                  loss=None, lse=None, loss_mean=None, stream=None):
+    """Merge [T, n] statistics -> (loss [n], lse [n], loss_mean [1]), fp32."""
+    for t, nm in ((m, "m"), (s, "s"), (zy, "zy")):
+        _need(t, torch.float32, 2, nm)
+    _need(targets, torch.int64, 1, "targets")
+    T, n = m.shape
+    if s.shape != (T, n) or zy.shape != (T, n) or targets.shape[0] != n:
+        raise ValueError("m, s, zy must be [T, n] and targets [n]")
+    dev = m.device
+    loss = torch.empty(n, dtype=torch.float32, device=dev) if loss is None else loss
+    lse = torch.empty(n, dtype=torch.float32, device=dev) if lse is None else lse
+    loss_mean = torch.empty(1, dtype=torch.float32, device=dev) if loss_mean is None else loss_mean
+    _check(lib.vp_ce_combine(_ptr(m), _ptr(s), _ptr(zy), _ptr(targets), n, T, int(ignore_index),
+                             _ptr(loss), _ptr(lse), _ptr(loss_mean), _stream(stream)),
+           "vp_ce_combine")
+    return loss, lse, loss_mean
+
+
+def vp_lmhead_ce_bwd(hidden, w_shard, targets, lse, vocab_start: int, vocab_end: int,
+                     grad_scale: float, ignore_index: int = DEFAULT_IGNORE_INDEX,
+                     dx=None, dw=None, workspace=None, stream=None):
+    """(dx partial [n, h], dw [Vs, h]) in fp32 for one shard."""
+    _need(hidden, torch.bfloat16, 2, "hidden")
+    _need(w_shard, torch.bfloat16, 2, "w_shard")
+    _need(targets, torch.int64, 1, "targets")
+    _need(lse, torch.float32, 1, "lse")
+    n, h = hidden.shape
+    vs = vocab_end - vocab_start
+    if w_shard.shape != (vs, h) or targets.shape[0] != n or lse.shape[0] != n:
+        raise ValueError("shape mismatch between hidden, w_shard, targets, lse and the vocab range")
+    dev = hidden.device
+    dx = torch.empty((n, h), dtype=torch.float32, device=dev) if dx is None else dx
+    dw = torch.empty((vs, h), dtype=torch.float32, device=dev) if dw is None else dw
+    _need(dx, torch.float32, 2, "dx")
+    _need(dw, torch.float32, 2, "dw")
+    need = vp_lmhead_ce_bwd_workspace(n, h, vocab_start, vocab_end)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib.vp_lmhead_ce_bwd(_ptr(hidden), _ptr(w_shard), _ptr(targets), _ptr(lse), n, h,
+                                int(vocab_start), int(vocab_end), int(ignore_index),
+                                float(grad_scale), _ptr(dx), _ptr(dw), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)),
+           "vp_lmhead_ce_bwd")
+    return dx, dw

@@ -1,0 +1,133 @@
+// C ABI of the vocab-parallel LM head + cross entropy (declared in include/vp_lmhead.h).
+//
+// Every entry point validates its arguments on the host, before anything is
+// launched, then enqueues its kernels on the caller's stream and returns
+// without synchronising.  No exception crosses this boundary.
+#include "vp_lmhead.h"
+
+#include <stdint.h>
+
+#include "launch.hpp"
+
+namespace {
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shared checks of a (hidden, weight shard) pair.
+int check_shard(int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end) {
+    if (n < 0 || h <= 0) return VP_ERR_SHAPE;
+    if (vocab_start < 0 || vocab_end <= vocab_start) return VP_ERR_RANGE;
+    // the GEMM tiling indexes rows and columns with 32-bit integers
+    if (n > INT32_MAX / 2 || h > INT32_MAX / 2 || vocab_end - vocab_start > INT32_MAX / 2)
+        return VP_ERR_SHAPE;
+    if (h % 8 != 0) return VP_ERR_ALIGN;
+    return VP_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? VP_OK : VP_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *vp_status_string(int status) {
+    switch (status) {
+        case VP_OK: return "VP_OK";
+        case VP_ERR_NULL: return "VP_ERR_NULL: a required pointer is null";
+        case VP_ERR_SHAPE: return "VP_ERR_SHAPE: invalid size (negative, zero, too large, or V % T != 0)";
+        case VP_ERR_RANGE: return "VP_ERR_RANGE: invalid vocabulary interval or shard index";
+        case VP_ERR_ALIGN: return "VP_ERR_ALIGN: h must be a multiple of 8 and tensors 16-byte aligned";
+        case VP_ERR_WORKSPACE: return "VP_ERR_WORKSPACE: workspace missing or too small";
+        case VP_ERR_HIP: return "VP_ERR_HIP: the HIP runtime reported a launch error";
+        default: return "unknown vp_status";
+    }
+}
+
+int vp_shard_range(int64_t V, int32_t T, int32_t t, int64_t *start, int64_t *end) {
+    if (!start || !end) return VP_ERR_NULL;
+    if (V <= 0 || T < 1 || V % T != 0) return VP_ERR_SHAPE;
+    if (t < 0 || t >= T) return VP_ERR_RANGE;
+    const int64_t vs = V / T;
+    *start = (int64_t)t * vs;
+    *end = *start + vs;
+    return VP_OK;
+}
+
+int vp_embed_fwd(const int64_t *ids, int64_t n, const uint16_t *w_shard, int64_t vocab_start,
+                 int64_t vocab_end, int64_t h, uint16_t *out, hipStream_t stream) {
+    if (n < 0 || h <= 0) return VP_ERR_SHAPE;
+    if (vocab_start < 0 || vocab_end <= vocab_start) return VP_ERR_RANGE;
+    if (h % 8 != 0) return VP_ERR_ALIGN;
+    if (n == 0) return VP_OK;
+    if (!ids || !w_shard || !out) return VP_ERR_NULL;
+    if (!aligned(ids, 8) || !aligned(w_shard, 16) || !aligned(out, 16)) return VP_ERR_ALIGN;
+    return hip_status(vp::launch_embed(ids, n, w_shard, vocab_start, vocab_end, h, out, stream));
+}
+
+size_t vp_lmhead_ce_fwd_workspace(int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end) {
+    if (check_shard(n, h, vocab_start, vocab_end) != VP_OK || n == 0) return 0;
+    return vp::fwd_workspace(n, vocab_end - vocab_start).bytes;
+}
+
+int vp_lmhead_ce_fwd(const uint16_t *hidden, const uint16_t *w_shard, const int64_t *targets,
+                     int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end, float *m_local,
+                     float *s_local, float *zy_local, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+    int st = check_shard(n, h, vocab_start, vocab_end);
+    if (st != VP_OK) return st;
+    if (n == 0) return VP_OK;
+    if (!hidden || !w_shard || !targets || !m_local || !s_local || !zy_local) return VP_ERR_NULL;
+    if (!aligned(hidden, 16) || !aligned(w_shard, 16) || !aligned(targets, 8) ||
+        !aligned(m_local, 4) || !aligned(s_local, 4) || !aligned(zy_local, 4))
+        return VP_ERR_ALIGN;
+    const int64_t vs = vocab_end - vocab_start;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < vp::fwd_workspace(n, vs).bytes)
+        return VP_ERR_WORKSPACE;
+    return hip_status(vp::launch_ce_fwd(hidden, w_shard, targets, n, h, vocab_start, vs, m_local,
+                                        s_local, zy_local, workspace, stream));
+}
+
+int vp_ce_combine(const float *m, const float *s, const float *zy, const int64_t *targets,
+                  int64_t n, int32_t T, int64_t ignore_index, float *loss, float *lse,
+                  float *loss_mean, hipStream_t stream) {
+    if (n < 0 || T < 1 || n > INT64_MAX / T) return VP_ERR_SHAPE;
+    if (!loss_mean) return VP_ERR_NULL;
+    if (n > 0) {
+        if (!m || !s || !zy || !targets || !loss || !lse) return VP_ERR_NULL;
+        if (!aligned(m, 4) || !aligned(s, 4) || !aligned(zy, 4) || !aligned(targets, 8) ||
+            !aligned(loss, 4) || !aligned(lse, 4))
+            return VP_ERR_ALIGN;
+    }
+    if (!aligned(loss_mean, 4)) return VP_ERR_ALIGN;
+    return hip_status(
+        vp::launch_ce_combine(m, s, zy, targets, n, T, ignore_index, loss, lse, loss_mean, stream));
+}
+
+size_t vp_lmhead_ce_bwd_workspace(int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end) {
+    if (check_shard(n, h, vocab_start, vocab_end) != VP_OK || n == 0) return 0;
+    return vp::bwd_workspace(n, h, vocab_end - vocab_start).bytes;
+}
+
+int vp_lmhead_ce_bwd(const uint16_t *hidden, const uint16_t *w_shard, const int64_t *targets,
+                     const float *lse, int64_t n, int64_t h, int64_t vocab_start,
+                     int64_t vocab_end, int64_t ignore_index, float grad_scale, float *dx,
+                     float *dw, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    int st = check_shard(n, h, vocab_start, vocab_end);
+    if (st != VP_OK) return st;
+    const int64_t vs = vocab_end - vocab_start;
+    if (!dw) return VP_ERR_NULL;
+    if (!aligned(dw, 16)) return VP_ERR_ALIGN;
+    if (n > 0) {
+        if (!hidden || !w_shard || !targets || !lse || !dx) return VP_ERR_NULL;
+        if (!aligned(hidden, 16) || !aligned(w_shard, 16) || !aligned(targets, 8) ||
+            !aligned(lse, 4) || !aligned(dx, 16))
+            return VP_ERR_ALIGN;
+        if (!workspace || !aligned(workspace, 256) ||
+            workspace_bytes < vp::bwd_workspace(n, h, vs).bytes)
+            return VP_ERR_WORKSPACE;
+    }
+    return hip_status(vp::launch_ce_bwd(hidden, w_shard, targets, lse, n, h, vocab_start, vs,
+                                        ignore_index, grad_scale, dx, dw, workspace, stream));
+}
+
+}  // extern "C"

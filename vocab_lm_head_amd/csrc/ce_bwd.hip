@@ -1,0 +1,222 @@
+// Local backward of one vocabulary shard.
+//
+// Method: MiniMind-Tron "5 Vocab Parallelism", 5.3.2 -- dCE/dz_j = p_j - [j == y],
+// with p from the local logits and the global log-sum-exp, and the one-hot
+// subtracted only on the shard that owns the target; no communication.  5.3.3:
+// ignored tokens get zero gradient and the mean divides by max(1, N_valid).
+// The input gradient of this shard is a partial sum (column-parallel linear,
+// glossary "Tensor Parallelism"); the weight gradient is local.
+//
+// Steps (all on the caller's stream):
+//   1. X -> X^T and W_r -> W_r^T (bf16, zero-padded to a multiple of 8 columns),
+//      so that all three GEMMs are K-contiguous on both operands;
+//   2. recompute z^T = W_r X^T on MFMA; the epilogue forms
+//      dz = g (exp(z - lse) - onehot) in registers and writes it in bf16 twice,
+//      token-major dz [N, Vs8] and vocab-major dz^T [Vs, N8];
+//   3. dX_r^T = W_r^T dz^T  (A = W_r^T [H, Vs8], B = dz [N, Vs8]),   K = Vs
+//   4. dW_r^T = X^T dz      (A = X^T [H, N8],    B = dz^T [Vs, N8]), K = N
+// The [N, Vs] dlogits must reach memory once: a register-only fusion of dX and
+// dW would need fp32 atomics on [tile, H] slabs for every tile, far below the
+// MFMA roofline at H = 4096.
+#include <algorithm>
+
+#include "gemm.hpp"
+#include "launch.hpp"
+
+namespace vp {
+
+namespace {
+
+// out[c, r] = in[r, c] for r < rows, c < cols; out[c, r] = 0 for rows <= r < ld_out.
+// in: [rows, cols] row-major (cols multiple of 8); out: [cols, ld_out] (ld_out multiple of 8).
+constexpr int kTT = 64;
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ in,
+                                                             int64_t rows, int64_t cols,
+                                                             uint16_t *__restrict__ out,
+                                                             int64_t ld_out) {
+    __shared__ uint16_t tile[kTT][kTT + 2];
+    const int64_t r0 = (int64_t)blockIdx.x * kTT;   // input rows  = output columns
+    const int64_t c0 = (int64_t)blockIdx.y * kTT;   // input cols  = output rows
+    const int t = threadIdx.x;
+    {
+        const int r = t >> 2, cc = (t & 3) * 16;
+        const int64_t gr = r0 + r;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t gc = c0 + cc + 8 * half;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (gr < rows && gc < cols) v = *(const u32x4 *)(in + gr * cols + gc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                tile[r][cc + 8 * half + 2 * q] = (uint16_t)(v[q] & 0xFFFFu);
+                tile[r][cc + 8 * half + 2 * q + 1] = (uint16_t)(v[q] >> 16);
+            }
+        }
+    }
+    __syncthreads();
+    {
+        const int oc = t >> 2, rr = (t & 3) * 16;   // output row c0 + oc, output cols r0 + rr ..
+        const int64_t grow = c0 + oc;
+        if (grow >= cols) return;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t gcol = r0 + rr + 8 * half;
+            if (gcol >= ld_out) continue;
+            u32x4 v;   // rows past `rows` were staged as zeros
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                v[q] = (unsigned)tile[rr + 8 * half + 2 * q][oc] |
+                       ((unsigned)tile[rr + 8 * half + 2 * q + 1][oc] << 16);
+            *(u32x4 *)(out + grow * ld_out + gcol) = v;
+        }
+    }
+}
+
+hipError_t transpose_bf16(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out,
+                          int64_t ld_out, hipStream_t stream) {
+    dim3 grid((unsigned)ceil_div(ld_out, kTT), (unsigned)ceil_div(cols, kTT));
+    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, stream, in, rows, cols, out, ld_out);
+    return hipGetLastError();
+}
+
+// dz = g (softmax - onehot) from the recomputed z^T tile; rows = vocab, cols = tokens.
+struct DlogitsEpilogue {
+    const int64_t *targets;
+    const float *lse;
+    int64_t start;
+    int64_t ignore_index;
+    float grad_scale;
+    int M, N;              // Vs, tokens
+    int64_t M8, N8;        // padded leading dims
+    uint16_t *dz;          // [N, M8]
+    uint16_t *dzt;         // [M, N8]
+
+    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane) const {
+        const int rsub = 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int n = nbase + 16 * j + (lane & 15);
+            const bool ncol = n < N;
+            float g = 0.f, lsel = 0.f;
+            int64_t trow = -1;
+            if (ncol) {
+                const int64_t y = targets[n];
+                g = (y == ignore_index) ? 0.f : grad_scale;
+                lsel = lse[n] * kLog2e;
+                trow = y - start;
+            }
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const int row0 = mbase + 16 * i + rsub;   // vocabulary row of r = 0
+                float d[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = fast_exp2(fmaf(acc[i][j][r], kLog2e, -lsel));
+                    const float v = g * (p - ((row0 + r) == trow ? 1.f : 0.f));
+                    d[r] = (ncol && (row0 + r) < M) ? v : 0.f;   // padding stays exactly 0
+                }
+                if (ncol && row0 < M8)
+                    *(u32x2 *)(dz + (int64_t)n * M8 + row0) = pack_bf16x4(d[0], d[1], d[2], d[3]);
+                if (n < N8) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (row0 + r < M) dzt[(int64_t)(row0 + r) * N8 + n] = bf16_bits(d[r]);
+                }
+            }
+        }
+    }
+};
+
+// out[n, m] = C[m, n] (fp32), m < M, n < N; M a multiple of 4.
+struct StoreTransposedEpilogue {
+    float *out;
+    int64_t ldo;
+    int M, N;
+
+    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane) const {
+        const int rsub = 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int n = nbase + 16 * j + (lane & 15);
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const int m = mbase + 16 * i + rsub;
+                if (m < M) *(f32x4 *)(out + (int64_t)n * ldo + m) = acc[i][j];
+            }
+        }
+    }
+};
+
+__global__ void fill_zero_kernel(float *p, int64_t count) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.f;
+}
+
+}  // namespace
+
+BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs) {
+    BwdWorkspace b;
+    b.n8 = round_up(n, 8);
+    b.vs8 = round_up(vs, 8);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (size_t)round_up((int64_t)bytes, 256);
+        return o;
+    };
+    b.off_xt = take((size_t)h * b.n8 * 2);
+    b.off_wt = take((size_t)h * b.vs8 * 2);
+    b.off_dz = take((size_t)n * b.vs8 * 2);
+    b.off_dzt = take((size_t)vs * b.n8 * 2);
+    b.bytes = off;
+    return b;
+}
+
+hipError_t launch_ce_bwd(const uint16_t *x, const uint16_t *w, const int64_t *targets,
+                         const float *lse, int64_t n, int64_t h, int64_t start, int64_t vs,
+                         int64_t ignore_index, float grad_scale, float *dx, float *dw, void *ws,
+                         hipStream_t stream) {
+    if (n == 0) {   // no tokens: the weight gradient is zero, dx has no rows
+        const int64_t cnt = vs * h;
+        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(cnt, 256), 8192)),
+                           dim3(256), 0, stream, dw, cnt);
+        return hipGetLastError();
+    }
+    const BwdWorkspace b = bwd_workspace(n, h, vs);
+    char *base = (char *)ws;
+    uint16_t *xt = (uint16_t *)(base + b.off_xt);
+    uint16_t *wt = (uint16_t *)(base + b.off_wt);
+    uint16_t *dz = (uint16_t *)(base + b.off_dz);
+    uint16_t *dzt = (uint16_t *)(base + b.off_dzt);
+    hipError_t e;
+    if ((e = transpose_bf16(x, n, h, xt, b.n8, stream)) != hipSuccess) return e;
+    if ((e = transpose_bf16(w, vs, h, wt, b.vs8, stream)) != hipSuccess) return e;
+
+    {   // recompute + dlogits: rows = vocab (A = W_r), cols = tokens (B = X)
+        const GemmGrid g = gemm_grid(vs, n);
+        DlogitsEpilogue epi{targets, lse, start, ignore_index, grad_scale, (int)vs, (int)n,
+                            b.vs8, b.n8, dz, dzt};
+        hipLaunchKernelGGL(gemm_nt_kernel<DlogitsEpilogue>, dim3(g.blocks()), dim3(kThreads), 0,
+                           stream, Operand{w, h, (int)vs}, Operand{x, h, (int)n}, (int)h,
+                           g.tiles_m, g.tiles_n, epi);
+    }
+    {   // dX_r^T [H, N] = W_r^T [H, Vs8] . dz [N, Vs8]^T
+        const GemmGrid g = gemm_grid(h, n);
+        StoreTransposedEpilogue epi{dx, h, (int)h, (int)n};
+        hipLaunchKernelGGL(gemm_nt_kernel<StoreTransposedEpilogue>, dim3(g.blocks()), dim3(kThreads),
+                           0, stream, Operand{wt, b.vs8, (int)h}, Operand{dz, b.vs8, (int)n},
+                           (int)b.vs8, g.tiles_m, g.tiles_n, epi);
+    }
+    {   // dW_r^T [H, Vs] = X^T [H, N8] . dz^T [Vs, N8]^T
+        const GemmGrid g = gemm_grid(h, vs);
+        StoreTransposedEpilogue epi{dw, h, (int)h, (int)vs};
+        hipLaunchKernelGGL(gemm_nt_kernel<StoreTransposedEpilogue>, dim3(g.blocks()), dim3(kThreads),
+                           0, stream, Operand{xt, b.n8, (int)h}, Operand{dzt, b.n8, (int)vs},
+                           (int)b.n8, g.tiles_m, g.tiles_n, epi);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace vp

@@ -1,0 +1,44 @@
+// Internal launchers behind the C ABI.  Arguments are validated by api.cpp
+// before any of these is called; each returns hipGetLastError() after its
+// launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vp {
+
+// forward workspace: fp32 partial (max, sum-exp, target logit) per 128-row
+// vocabulary slice and token
+struct FwdWorkspace {
+    int64_t slices;        // ceil(Vs / 128)
+    size_t bytes;
+};
+FwdWorkspace fwd_workspace(int64_t n, int64_t vs);
+
+// backward workspace: X^T [H, N8], W^T [H, Vs8], dz [N, Vs8], dz^T [Vs, N8] (bf16)
+struct BwdWorkspace {
+    int64_t n8, vs8;
+    size_t off_xt, off_wt, off_dz, off_dzt;
+    size_t bytes;
+};
+BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs);
+
+hipError_t launch_embed(const int64_t *ids, int64_t n, const uint16_t *w, int64_t start,
+                        int64_t end, int64_t h, uint16_t *out, hipStream_t stream);
+
+hipError_t launch_ce_fwd(const uint16_t *x, const uint16_t *w, const int64_t *targets, int64_t n,
+                         int64_t h, int64_t start, int64_t vs, float *m_out, float *s_out,
+                         float *zy_out, void *ws, hipStream_t stream);
+
+hipError_t launch_ce_combine(const float *m, const float *s, const float *zy,
+                             const int64_t *targets, int64_t n, int T, int64_t ignore_index,
+                             float *loss, float *lse, float *loss_mean, hipStream_t stream);
+
+hipError_t launch_ce_bwd(const uint16_t *x, const uint16_t *w, const int64_t *targets,
+                         const float *lse, int64_t n, int64_t h, int64_t start, int64_t vs,
+                         int64_t ignore_index, float grad_scale, float *dx, float *dw, void *ws,
+                         hipStream_t stream);
+
+}  // namespace vp
