@@ -25,7 +25,11 @@ SOURCES = ["api.cpp", "embed.hip", "ce_fwd.hip", "ce_combine.hip", "ce_bwd.hip"]
 
 # packed-fp32 VALU forms are disabled on purpose: the compiler would otherwise
 # emit them from plain float code in the epilogues.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The "iterative-minreg" machine scheduler keeps each of the GEMM's 256 fp32
+# accumulators in one AGPR across the K loop; the default strategy splits their
+# live ranges and adds ~140 v_accvgpr copies per 128 MFMAs.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]
 
 
 def hipcc() -> str:

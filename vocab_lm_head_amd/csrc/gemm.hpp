@@ -16,13 +16,15 @@
 // LDS rows are 64 bf16 = 128 B = eight 16-byte chunks; chunk c of row r is
 // stored at chunk c ^ (r & 7) so that the 16-lane groups of a fragment read
 // (16 consecutive rows, one chunk) hit distinct banks.
-// Global -> LDS staging goes through registers: the loads of step k+1 are
-// issued before the MFMAs of step k and written to the other LDS buffer
-// after them, with one barrier per K step.
+// Global -> LDS goes through buffer loads straight into LDS (buffer_load ... lds),
+// two K steps ahead; operand fragments are double-buffered in registers so
+// that the LDS reads of one half K step overlap the MFMAs of the other; one
+// barrier per K step.
 //
-// Rows past M / N are clamped to the last row (their results are masked by
-// the epilogue); K chunks past K are zero-filled, so K need only be a multiple
-// of 8.  Operands must have 16-byte aligned rows.
+// Rows past M / N read as zeros (outside the buffer resource; the epilogue
+// masks them); K chunks past K are zero-filled, so K need only be a multiple
+// of 8.  Operands must have 16-byte aligned rows, and a 256-row panel must
+// stay below 2 GiB (ld < 4M elements) so that byte offsets fit 32 bits.
 #pragma once
 
 #include "common.hpp"
@@ -38,6 +40,8 @@ constexpr int kWN = 128;           // wave tile cols
 constexpr int kTM = kWM / 16;      // MFMA tiles per wave along M
 constexpr int kTN = kWN / 16;      // MFMA tiles per wave along N
 constexpr int kGroupM = 8;         // tiles per raster group along M
+// s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8])
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 struct Operand {
     const uint16_t *p;   // row-major [rows, K] bf16 bits
@@ -65,38 +69,84 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
 
 typedef f32x4 Acc[kTM][kTN];
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// dword 3 of a gfx9 raw buffer resource (32-bit data format; no swizzle, no index)
+constexpr int kBufferFlags = 0x00020000;
+// a buffer offset past any resource this kernel builds (they stay below 2 GiB)
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// One K step of operand fragments held by a wave: 8 A rows-blocks and 8 B col-blocks.
+struct Frags {
+    bf16x8 a[kTM];
+    bf16x8 b[kTN];
+};
+
 template <class Epilogue>
-__global__ __launch_bounds__(kThreads) void gemm_nt_kernel(Operand A, Operand B, int K,
-                                                           int tiles_m, int tiles_n, Epilogue epi) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2][(kBM + kBN) * kBK];
+__global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand B, int K,
+                                                              int tiles_m, int tiles_n,
+                                                              Epilogue epi) {
+    // two LDS stages of one [256 x 64] A tile and one [256 x 64] B tile each (2 x 64 KiB)
+    constexpr int kStage = (kBM + kBN) * kBK;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * kStage];
 
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * kBM, n0 = tn * kBN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int wm = wave & 1, wn = wave >> 1;
 
-    // staging map: 16-byte chunk c of rows rs + 32 i, i = 0..7, for A and for B
-    const int c = tid & 7, rs = tid >> 3;
-    const int kc = c * 8;
-    const int st_off = rs * kBK + ((c ^ (rs & 7)) * 8);   // LDS element offset of row rs
-    const uint16_t *a_row[8];
-    const uint16_t *b_row[8];
+    // Global -> LDS map (buffer loads straight into LDS, 16 bytes per lane).  One wave
+    // instruction fills 8 rows x 128 B = 1 KiB of LDS in lane order: lane L lands on
+    // row L/8, physical chunk L%8, so it fetches the logical chunk (L%8) ^ (row & 7).
+    // Wave w fills row groups 8w .. 8w+7 of A and of B (rows 64w .. 64w+63).
+    // The buffer resource starts at the tile's first row and ends at the tensor's
+    // end, so rows past M (or N) fall outside it and read as zeros.
+    const int lrow = lane >> 3;
+    const int lchunk = (lane & 7) ^ lrow;
+    const char *a_panel = (const char *)(A.p + (int64_t)m0 * A.ld);
+    const char *b_panel = (const char *)(B.p + (int64_t)n0 * B.ld);
+    // bytes from the panel start to the end of the last row (past it: zeros)
+    const uint32_t a_bytes = (uint32_t)((int64_t)(A.rows - m0) * A.ld * 2);
+    const uint32_t b_bytes = (uint32_t)((int64_t)(B.rows - n0) * B.ld * 2);
+    const uint32_t a_row8 = (uint32_t)(8 * A.ld * 2), b_row8 = (uint32_t)(8 * B.ld * 2);
+    const uint32_t a_off0 = (uint32_t)(((wave * 64 + lrow) * A.ld + lchunk * 8) * 2);
+    const uint32_t b_off0 = (uint32_t)(((wave * 64 + lrow) * B.ld + lchunk * 8) * 2);
+    const int grp = wave * 8 * 8 * kBK;   // LDS element offset of this wave's first row group
+
+    // Branch-free: a chunk at or past K (the last partial K step, or a step past the
+    // end) gets an offset outside the resource, which reads as zeros.
+    auto load_tile = [&](uint16_t *buf, int k0) {
+        const __amdgpu_buffer_rsrc_t ra =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(a_panel + 2 * k0), (short)0, a_bytes, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rb =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(b_panel + 2 * k0), (short)0, b_bytes, kBufferFlags);
+        const bool ok = k0 + lchunk * 8 < K;
+        const uint32_t oa = ok ? a_off0 : kOutOfRange;
+        const uint32_t ob = ok ? b_off0 : kOutOfRange;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int ra = min(m0 + rs + 32 * i, A.rows - 1);
-        const int rb = min(n0 + rs + 32 * i, B.rows - 1);
-        a_row[i] = A.p + (int64_t)ra * A.ld + kc;
-        b_row[i] = B.p + (int64_t)rb * B.ld + kc;
-    }
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(buf + grp + i * 8 * kBK), 16,
+                                                     oa + i * a_row8, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void *)(buf + kBM * kBK + grp + i * 8 * kBK), 16, ob + i * b_row8, 0, 0, 0);
+        }
+    };
 
     // fragment map: lane reads row (lane & 15) of each 16-row tile, logical chunk kk*4 + lane/16
     const int fr = lane & 15;
-    int frag_off[2];
+    const int a_off = (wm * kWM + fr) * kBK;
+    const int b_off = kBM * kBK + (wn * kWN + fr) * kBK;
+    const int ch0 = ((0 + (lane >> 4)) ^ (fr & 7)) * 8;
+    const int ch1 = ((4 + (lane >> 4)) ^ (fr & 7)) * 8;
+
+    auto read_frags = [&](const uint16_t *buf, int ch, Frags &f) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) frag_off[kk] = fr * kBK + (((kk * 4 + (lane >> 4)) ^ (fr & 7)) * 8);
-    const int a_base = (wm * kWM) * kBK;
-    const int b_base = kBM * kBK + (wn * kWN) * kBK;
+        for (int i = 0; i < kTM; ++i) f.a[i] = *(const bf16x8 *)&buf[a_off + i * 16 * kBK + ch];
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) f.b[j] = *(const bf16x8 *)&buf[b_off + j * 16 * kBK + ch];
+    };
 
     Acc acc;
 #pragma unroll
@@ -104,48 +154,57 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(Operand A, Operand B,
 #pragma unroll
         for (int j = 0; j < kTN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 sa[8], sb[8];
-    auto gload = [&](int k0) {
-        const bool ok = (k0 + kc) < K;
+    auto mma = [&](const Frags &f, int i0, int i1) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            sa[i] = ok ? *(const u32x4 *)(a_row[i] + k0) : u32x4{0u, 0u, 0u, 0u};
-            sb[i] = ok ? *(const u32x4 *)(b_row[i] + k0) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto lstore = [&](int buf) {
+        for (int i = i0; i < i1; ++i)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            *(u32x4 *)&smem[buf][st_off + 32 * i * kBK] = sa[i];
-            *(u32x4 *)&smem[buf][kBM * kBK + st_off + 32 * i * kBK] = sb[i];
-        }
+            for (int j = 0; j < kTN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     };
 
     const int KT = (int)ceil_div(K, kBK);
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    Frags f0, f1;
 
+    load_tile(smem, 0);
+    load_tile(smem + kStage, kBK);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    read_frags(smem, ch0, f0);
+
+    // K step kt works on the tile in stage kt & 1; the next tile is in the other stage.
+    // F0 (K 0..31 of the step) is already in registers when the step starts.  The
+    // sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read, 0x020 global/buffer load.
     for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) gload((kt + 1) * kBK);
-        const uint16_t *S = smem[cur];
+        uint16_t *cur = smem + (kt & 1) * kStage;
+        uint16_t *nxt = smem + ((kt + 1) & 1) * kStage;
+        // phase 1: F0's 64 MFMAs, with F1's 16 LDS reads spread over the first 32
+        read_frags(cur, ch1, f1);
+        mma(f0, 0, kTM);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 af[kTM], bfr[kTN];
-#pragma unroll
-            for (int i = 0; i < kTM; ++i) af[i] = *(const bf16x8 *)&S[a_base + i * 16 * kBK + frag_off[kk]];
-#pragma unroll
-            for (int j = 0; j < kTN; ++j) bfr[j] = *(const bf16x8 *)&S[b_base + j * 16 * kBK + frag_off[kk]];
-#pragma unroll
-            for (int i = 0; i < kTM; ++i)
-#pragma unroll
-                for (int j = 0; j < kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        if (more) lstore(cur ^ 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // every wave has its F1 (nobody reads `cur` any more) and tile kt+1 has landed;
+        // no branch: past the last step the loads read zeros and F0 is unused
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        // phase 2: F1's 64 MFMAs, with tile kt+2's 16 loads and the next F0's 16 reads
+        load_tile(cur, (kt + 2) * kBK);
+        read_frags(nxt, ch0, f0);
+        mma(f1, 0, kTM);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // accumulator layout of v_mfma_f32_16x16x32: acc[i][j][r] is
