@@ -11,8 +11,8 @@
 //   1. X -> X^T and W_r -> W_r^T (bf16, zero-padded to a multiple of 8 columns),
 //      so that all three GEMMs are K-contiguous on both operands;
 //   2. recompute z^T = W_r X^T on MFMA; the epilogue forms
-//      dz = g (exp(z - lse) - onehot) in registers and writes it in bf16 twice,
-//      token-major dz [N, Vs8] and vocab-major dz^T [Vs, N8];
+//      dz = g (exp(z - lse) - onehot) in registers, stages the tile in LDS and
+//      writes it in bf16 twice, token-major dz [N, Vs8] and vocab-major dz^T [Vs, N8];
 //   3. dX_r^T = W_r^T dz^T  (A = W_r^T [H, Vs8], B = dz [N, Vs8]),   K = Vs
 //   4. dW_r^T = X^T dz      (A = X^T [H, N8],    B = dz^T [Vs, N8]), K = N
 // The [N, Vs] dlogits must reach memory once: a register-only fusion of dX and
@@ -80,6 +80,20 @@ hipError_t transpose_bf16(const uint16_t *in, int64_t rows, int64_t cols, uint16
 }
 
 // dz = g (softmax - onehot) from the recomputed z^T tile; rows = vocab, cols = tokens.
+// The 256 x 256 bf16 tile is staged in the GEMM's LDS as [token][vocab] rows of
+// 512 bytes, then written out with 16-byte coalesced stores twice: token-major
+// dz [N, M8] and vocab-major dz^T [M, N8].  Padding columns (vocab >= M,
+// token >= N) are written as zeros.
+static_assert(kBN * kBM <= 2 * (kBM + kBN) * kBK, "dz tile must fit the GEMM's LDS");
+
+// Element offset of (row, col) in the staged tile: 16-byte chunks are XOR-swizzled
+// with (row ^ row/8) so that 16 consecutive rows at one column (the MFMA-layout
+// writes) and rows 8 apart at one column (the vocab-major reads) fall in
+// different banks, while a row read stays one contiguous permuted row.
+__device__ __forceinline__ int dz_swz(int row, int col) {
+    return row * kBM + ((((col >> 3) ^ ((row ^ (row >> 3)) & 31)) << 3) | (col & 7));
+}
+
 struct DlogitsEpilogue {
     const int64_t *targets;
     const float *lse;
@@ -91,7 +105,8 @@ struct DlogitsEpilogue {
     uint16_t *dz;          // [N, M8]
     uint16_t *dzt;         // [M, N8]
 
-    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane) const {
+    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane, int m0,
+                                               int n0, uint16_t *lds) const {
         const int rsub = 4 * (lane >> 4);
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
@@ -115,13 +130,39 @@ struct DlogitsEpilogue {
                     const float v = g * (p - ((row0 + r) == trow ? 1.f : 0.f));
                     d[r] = (ncol && (row0 + r) < M) ? v : 0.f;   // padding stays exactly 0
                 }
-                if (ncol && row0 < M8)
-                    *(u32x2 *)(dz + (int64_t)n * M8 + row0) = pack_bf16x4(d[0], d[1], d[2], d[3]);
-                if (n < N8) {
+                *(u32x2 *)(lds + dz_swz(n - n0, row0 - m0)) = pack_bf16x4(d[0], d[1], d[2], d[3]);
+            }
+        }
+        __syncthreads();
+        const int t = threadIdx.x;
+        // token-major: 256 rows x 32 chunks of 16 B; a wave covers two rows per instruction
+#pragma unroll 4
+        for (int it = 0; it < (kBN * kBM / 8) / kThreads; ++it) {
+            const int q = it * kThreads + t;
+            const int r = q >> 5, c = (q & 31) * 8;
+            const int n = n0 + r;
+            if (n < N && m0 + c < M8)
+                *(u32x4 *)(dz + (int64_t)n * M8 + m0 + c) = *(const u32x4 *)(lds + dz_swz(r, c));
+        }
+        // vocab-major: a lane gathers 4 vocab rows x 8 tokens (eight 8-byte LDS reads) and
+        // writes four 16-byte chunks; 32 lanes cover 512 contiguous bytes of each row
+#pragma unroll 2
+        for (int it = 0; it < (kBM * kBN / 32) / kThreads; ++it) {
+            const int q = it * kThreads + t;
+            const int v0 = (q >> 5) * 4, c = (q & 31) * 8;   // first vocab row, first token
+            if (n0 + c >= N8 || m0 + v0 >= M) continue;
+            u32x2 rd[8];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (row0 + r < M) dzt[(int64_t)(row0 + r) * N8 + n] = bf16_bits(d[r]);
-                }
+            for (int e = 0; e < 8; ++e) rd[e] = *(const u32x2 *)(lds + dz_swz(c + e, v0));
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                if (m0 + v0 + v >= M) break;
+                const int w = v >> 1, sh = (v & 1) * 16;
+                u32x4 o;
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    o[p] = ((rd[2 * p][w] >> sh) & 0xFFFFu) | (((rd[2 * p + 1][w] >> sh) & 0xFFFFu) << 16);
+                *(u32x4 *)(dzt + (int64_t)(m0 + v0 + v) * N8 + n0 + c) = o;
             }
         }
     }
@@ -133,7 +174,8 @@ struct StoreTransposedEpilogue {
     int64_t ldo;
     int M, N;
 
-    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane) const {
+    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane, int, int,
+                                               uint16_t *) const {
         const int rsub = 4 * (lane >> 4);
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {

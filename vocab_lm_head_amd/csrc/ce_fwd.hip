@@ -25,7 +25,8 @@ struct CeStatsEpilogue {
     float *part;          // [3][slices][N]: max, sum-exp, target logit
     int64_t slices;
 
-    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane) const {
+    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane, int, int,
+                                               uint16_t *) const {
         if (mbase >= M) return;                   // wave tile entirely past the shard
         const bool full = mbase + kWM <= M;
         const int rsub = 4 * (lane >> 4);
@@ -37,7 +38,7 @@ struct CeStatsEpilogue {
         for (int j = 0; j < kTN; ++j) {
             const int n = nbase + 16 * j + (lane & 15);
             // target row relative to this wave tile; -1 unless the target lies in the shard
-            // (rows past the shard's end exist in the last tile but hold clamped data)
+            // (rows past the shard's end exist in the last tile but hold no shard data)
             int64_t trow = -1;
             if (n < N) {
                 const int64_t local = targets[n] - start;
@@ -77,29 +78,43 @@ struct CeStatsEpilogue {
     }
 };
 
-// Merge the shard's per-slice partials of each token (one thread per token).
-__global__ __launch_bounds__(256) void merge_slices_kernel(const float *__restrict__ part,
-                                                           int64_t slices, int64_t n,
-                                                           float *__restrict__ m_out,
-                                                           float *__restrict__ s_out,
-                                                           float *__restrict__ zy_out) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
+// Merge the shard's per-slice partials of each token.  A workgroup takes 32
+// tokens; its 8 thread groups each merge every 8th slice (independent loads
+// in flight), then the 8 partial results are merged through LDS.
+constexpr int kMergeTok = 32, kMergeGrp = 8;
+__global__ __launch_bounds__(kMergeTok * kMergeGrp) void merge_slices_kernel(
+    const float *__restrict__ part, int64_t slices, int64_t n, float *__restrict__ m_out,
+    float *__restrict__ s_out, float *__restrict__ zy_out) {
+    __shared__ float sm[kMergeGrp][kMergeTok], ss[kMergeGrp][kMergeTok], sz[kMergeGrp][kMergeTok];
+    const int t = threadIdx.x % kMergeTok, g = threadIdx.x / kMergeTok;
+    const int64_t i = (int64_t)blockIdx.x * kMergeTok + t;
     float m = -INFINITY, s = 0.f, zy = 0.f;
-    for (int64_t p = 0; p < slices; ++p) {
-        const float mp = part[p * n + i];
-        const float sp = part[(slices + p) * n + i];
-        zy += part[(2 * slices + p) * n + i];
-        if (mp > m) {
-            s = s * fast_exp2((m - mp) * kLog2e) + sp;
-            m = mp;
-        } else {
-            s += sp * fast_exp2((mp - m) * kLog2e);
+    if (i < n) {
+        for (int64_t p = g; p < slices; p += kMergeGrp) {
+            const float mp = part[p * n + i];
+            const float sp = part[(slices + p) * n + i];
+            zy += part[(2 * slices + p) * n + i];
+            const float mx = fmaxf(m, mp);
+            s = s * fast_exp2((m - mx) * kLog2e) + sp * fast_exp2((mp - mx) * kLog2e);
+            m = mx;
         }
     }
-    m_out[i] = m;
-    s_out[i] = s;
-    zy_out[i] = zy;
+    sm[g][t] = m;
+    ss[g][t] = s;
+    sz[g][t] = zy;
+    __syncthreads();
+    if (g == 0 && i < n) {
+        float M = -INFINITY;
+        for (int q = 0; q < kMergeGrp; ++q) M = fmaxf(M, sm[q][t]);
+        float S = 0.f, Z = 0.f;
+        for (int q = 0; q < kMergeGrp; ++q) {
+            if (ss[q][t] != 0.f) S += ss[q][t] * fast_exp2((sm[q][t] - M) * kLog2e);
+            Z += sz[q][t];
+        }
+        m_out[i] = M;
+        s_out[i] = S;
+        zy_out[i] = Z;
+    }
 }
 
 }  // namespace
@@ -122,8 +137,8 @@ hipError_t launch_ce_fwd(const uint16_t *x, const uint16_t *w, const int64_t *ta
     Operand B{x, h, (int)n};
     hipLaunchKernelGGL(gemm_nt_kernel<CeStatsEpilogue>, dim3(g.blocks()), dim3(kThreads), 0, stream,
                        A, B, (int)h, g.tiles_m, g.tiles_n, epi);
-    hipLaunchKernelGGL(merge_slices_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream,
-                       part, fw.slices, n, m_out, s_out, zy_out);
+    hipLaunchKernelGGL(merge_slices_kernel, dim3((unsigned)ceil_div(n, kMergeTok)),
+                       dim3(kMergeTok * kMergeGrp), 0, stream, part, fw.slices, n, m_out, s_out, zy_out);
     return hipGetLastError();
 }
 

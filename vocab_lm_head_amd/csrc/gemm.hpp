@@ -207,9 +207,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    // The last steps' loads (zeros) may still be landing and other waves may still be
+    // reading: drain both before an epilogue reuses the LDS.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+
     // accumulator layout of v_mfma_f32_16x16x32: acc[i][j][r] is
     //   row m0 + wm*128 + 16 i + 4 (lane / 16) + r,  column n0 + wn*128 + 16 j + (lane % 16)
-    epi(acc, m0 + wm * kWM, n0 + wn * kWN, lane);
+    // The epilogue may use the 128 KiB of LDS (`smem`); all 256 threads call it.
+    epi(acc, m0 + wm * kWM, n0 + wn * kWN, lane, m0, n0, smem);
 }
 
 // Launch geometry of a GEMM over an M x N output.
