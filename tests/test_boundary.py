@@ -129,8 +129,10 @@ def test_bwd_validation_and_workspace(lib):
     n, h, vs = 8192, 4096, 16032
     need = ws(n, h, 0, vs)
     r256 = lambda b: -(-b // 256) * 256
-    assert need == r256(h * n * 2) + r256(h * vs * 2) + r256(n * vs * 2) + r256(vs * n * 2)
-    assert ws(6, 32, 0, 4) == r256(32 * 8 * 2) * 2 + r256(6 * 8 * 2) + r256(4 * 8 * 2)
+    r64 = lambda e: -(-e // 64) * 64      # rows padded to 64 elements
+    n64, vs64 = r64(n), r64(vs)
+    assert need == r256(h * n64 * 2) + r256(h * vs64 * 2) + r256(n * vs64 * 2) + r256(vs * n64 * 2)
+    assert ws(6, 32, 0, 4) == r256(32 * 64 * 2) * 2 + r256(6 * 64 * 2) + r256(4 * 64 * 2)
     f = lib.vp_lmhead_ce_bwd
     base = dict(x=FAKE, w=FAKE, t=FAKE, lse=FAKE, n=n, h=h, lo=0, hi=vs, ign=-100, g=1.0,
                 dx=FAKE, dw=FAKE, ws=FAKE, wsb=need)

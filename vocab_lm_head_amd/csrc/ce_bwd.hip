@@ -8,13 +8,13 @@
 // glossary "Tensor Parallelism"); the weight gradient is local.
 //
 // Steps (all on the caller's stream):
-//   1. X -> X^T and W_r -> W_r^T (bf16, zero-padded to a multiple of 8 columns),
-//      so that all three GEMMs are K-contiguous on both operands;
+//   1. X -> X^T and W_r -> W_r^T (bf16, rows zero-padded to a multiple of 64
+//      elements), so that all three GEMMs are K-contiguous on both operands;
 //   2. recompute z^T = W_r X^T on MFMA; the epilogue forms
 //      dz = g (exp(z - lse) - onehot) in registers, stages the tile in LDS and
-//      writes it in bf16 twice, token-major dz [N, Vs8] and vocab-major dz^T [Vs, N8];
-//   3. dX_r^T = W_r^T dz^T  (A = W_r^T [H, Vs8], B = dz [N, Vs8]),   K = Vs
-//   4. dW_r^T = X^T dz      (A = X^T [H, N8],    B = dz^T [Vs, N8]), K = N
+//      writes it in bf16 twice, token-major dz [N, Vs64] and vocab-major dz^T [Vs, N64];
+//   3. dX_r^T = W_r^T dz^T  (A = W_r^T [H, Vs64], B = dz [N, Vs64]), K = Vs64
+//   4. dW_r^T = X^T dz      (A = X^T [H, N64],   B = dz^T [Vs, N64]),  K = N64
 // The [N, Vs] dlogits must reach memory once: a register-only fusion of dX and
 // dW would need fp32 atomics on [tile, H] slabs for every tile, far below the
 // MFMA roofline at H = 4096.
@@ -82,7 +82,7 @@ hipError_t transpose_bf16(const uint16_t *in, int64_t rows, int64_t cols, uint16
 // dz = g (softmax - onehot) from the recomputed z^T tile; rows = vocab, cols = tokens.
 // The 256 x 256 bf16 tile is staged in the GEMM's LDS as [token][vocab] rows of
 // 512 bytes, then written out with 16-byte coalesced stores twice: token-major
-// dz [N, M8] and vocab-major dz^T [M, N8].  Padding columns (vocab >= M,
+// dz [N, ld_dz] and vocab-major dz^T [M, ld_dzt].  Padding columns (vocab >= M,
 // token >= N) are written as zeros.
 static_assert(kBN * kBM <= 2 * (kBM + kBN) * kBK, "dz tile must fit the GEMM's LDS");
 
@@ -101,9 +101,9 @@ struct DlogitsEpilogue {
     int64_t ignore_index;
     float grad_scale;
     int M, N;              // Vs, tokens
-    int64_t M8, N8;        // padded leading dims
-    uint16_t *dz;          // [N, M8]
-    uint16_t *dzt;         // [M, N8]
+    int64_t ld_dz, ld_dzt; // padded leading dims (multiples of 64)
+    uint16_t *dz;          // [N, ld_dz]
+    uint16_t *dzt;         // [M, ld_dzt]
 
     __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane, int m0,
                                                int n0, uint16_t *lds) const {
@@ -141,8 +141,8 @@ struct DlogitsEpilogue {
             const int q = it * kThreads + t;
             const int r = q >> 5, c = (q & 31) * 8;
             const int n = n0 + r;
-            if (n < N && m0 + c < M8)
-                *(u32x4 *)(dz + (int64_t)n * M8 + m0 + c) = *(const u32x4 *)(lds + dz_swz(r, c));
+            if (n < N && m0 + c < ld_dz)
+                *(u32x4 *)(dz + (int64_t)n * ld_dz + m0 + c) = *(const u32x4 *)(lds + dz_swz(r, c));
         }
         // vocab-major: a lane gathers 4 vocab rows x 8 tokens (eight 8-byte LDS reads) and
         // writes four 16-byte chunks; 32 lanes cover 512 contiguous bytes of each row
@@ -150,7 +150,7 @@ struct DlogitsEpilogue {
         for (int it = 0; it < (kBM * kBN / 32) / kThreads; ++it) {
             const int q = it * kThreads + t;
             const int v0 = (q >> 5) * 4, c = (q & 31) * 8;   // first vocab row, first token
-            if (n0 + c >= N8 || m0 + v0 >= M) continue;
+            if (n0 + c >= ld_dzt || m0 + v0 >= M) continue;
             u32x2 rd[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) rd[e] = *(const u32x2 *)(lds + dz_swz(c + e, v0));
@@ -162,7 +162,7 @@ struct DlogitsEpilogue {
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
                     o[p] = ((rd[2 * p][w] >> sh) & 0xFFFFu) | (((rd[2 * p + 1][w] >> sh) & 0xFFFFu) << 16);
-                *(u32x4 *)(dzt + (int64_t)(m0 + v0 + v) * N8 + n0 + c) = o;
+                *(u32x4 *)(dzt + (int64_t)(m0 + v0 + v) * ld_dzt + n0 + c) = o;
             }
         }
     }
@@ -200,18 +200,20 @@ __global__ void fill_zero_kernel(float *p, int64_t count) {
 
 BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs) {
     BwdWorkspace b;
-    b.n8 = round_up(n, 8);
-    b.vs8 = round_up(vs, 8);
+    // leading dimensions padded to 64 elements: every workspace row starts on a
+    // 128-byte line, so a 64-element K chunk of a GEMM operand is one line
+    b.n_ld = round_up(n, 64);
+    b.vs_ld = round_up(vs, 64);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
         off += (size_t)round_up((int64_t)bytes, 256);
         return o;
     };
-    b.off_xt = take((size_t)h * b.n8 * 2);
-    b.off_wt = take((size_t)h * b.vs8 * 2);
-    b.off_dz = take((size_t)n * b.vs8 * 2);
-    b.off_dzt = take((size_t)vs * b.n8 * 2);
+    b.off_xt = take((size_t)h * b.n_ld * 2);
+    b.off_wt = take((size_t)h * b.vs_ld * 2);
+    b.off_dz = take((size_t)n * b.vs_ld * 2);
+    b.off_dzt = take((size_t)vs * b.n_ld * 2);
     b.bytes = off;
     return b;
 }
@@ -233,30 +235,30 @@ hipError_t launch_ce_bwd(const uint16_t *x, const uint16_t *w, const int64_t *ta
     uint16_t *dz = (uint16_t *)(base + b.off_dz);
     uint16_t *dzt = (uint16_t *)(base + b.off_dzt);
     hipError_t e;
-    if ((e = transpose_bf16(x, n, h, xt, b.n8, stream)) != hipSuccess) return e;
-    if ((e = transpose_bf16(w, vs, h, wt, b.vs8, stream)) != hipSuccess) return e;
+    if ((e = transpose_bf16(x, n, h, xt, b.n_ld, stream)) != hipSuccess) return e;
+    if ((e = transpose_bf16(w, vs, h, wt, b.vs_ld, stream)) != hipSuccess) return e;
 
     {   // recompute + dlogits: rows = vocab (A = W_r), cols = tokens (B = X)
         const GemmGrid g = gemm_grid(vs, n);
         DlogitsEpilogue epi{targets, lse, start, ignore_index, grad_scale, (int)vs, (int)n,
-                            b.vs8, b.n8, dz, dzt};
+                            b.vs_ld, b.n_ld, dz, dzt};
         hipLaunchKernelGGL(gemm_nt_kernel<DlogitsEpilogue>, dim3(g.blocks()), dim3(kThreads), 0,
                            stream, Operand{w, h, (int)vs}, Operand{x, h, (int)n}, (int)h,
                            g.tiles_m, g.tiles_n, epi);
     }
-    {   // dX_r^T [H, N] = W_r^T [H, Vs8] . dz [N, Vs8]^T
+    {   // dX_r^T [H, N] = W_r^T [H, Vs64] . dz [N, Vs64]^T
         const GemmGrid g = gemm_grid(h, n);
         StoreTransposedEpilogue epi{dx, h, (int)h, (int)n};
         hipLaunchKernelGGL(gemm_nt_kernel<StoreTransposedEpilogue>, dim3(g.blocks()), dim3(kThreads),
-                           0, stream, Operand{wt, b.vs8, (int)h}, Operand{dz, b.vs8, (int)n},
-                           (int)b.vs8, g.tiles_m, g.tiles_n, epi);
+                           0, stream, Operand{wt, b.vs_ld, (int)h}, Operand{dz, b.vs_ld, (int)n},
+                           (int)b.vs_ld, g.tiles_m, g.tiles_n, epi);
     }
-    {   // dW_r^T [H, Vs] = X^T [H, N8] . dz^T [Vs, N8]^T
+    {   // dW_r^T [H, Vs] = X^T [H, ld_dzt] . dz^T [Vs, ld_dzt]^T
         const GemmGrid g = gemm_grid(h, vs);
         StoreTransposedEpilogue epi{dw, h, (int)h, (int)vs};
         hipLaunchKernelGGL(gemm_nt_kernel<StoreTransposedEpilogue>, dim3(g.blocks()), dim3(kThreads),
-                           0, stream, Operand{xt, b.n8, (int)h}, Operand{dzt, b.n8, (int)vs},
-                           (int)b.n8, g.tiles_m, g.tiles_n, epi);
+                           0, stream, Operand{xt, b.n_ld, (int)h}, Operand{dzt, b.n_ld, (int)vs},
+                           (int)b.n_ld, g.tiles_m, g.tiles_n, epi);
     }
     return hipGetLastError();
 }

@@ -9,10 +9,10 @@
 // so each lane's four accumulator rows are four consecutive elements of the
 // row-major output it stores (or the four vocabulary rows it reduces over).
 //
-// Tiling (one workgroup = 4 waves of 64 lanes, one workgroup per CU):
+// Tiling (one workgroup per CU, kWavesM x kWavesN waves of 64 lanes):
 //   block tile 256 (M) x 256 (N), K step 64, LDS double buffer 2 x 64 KiB;
-//   wave (wm, wn) owns a 128 x 128 sub-tile = 8 x 8 MFMA tiles of
-//   v_mfma_f32_16x16x32_bf16 with fp32 accumulators (256 per lane).
+//   wave (wm, wn) owns a kWM x kWN sub-tile = kTM x kTN MFMA tiles of
+//   v_mfma_f32_16x16x32_bf16 with fp32 accumulators (4 kTM kTN per lane).
 // LDS rows are 64 bf16 = 128 B = eight 16-byte chunks; chunk c of row r is
 // stored at chunk c ^ (r & 7) so that the 16-lane groups of a fragment read
 // (16 consecutive rows, one chunk) hit distinct banks.
@@ -34,11 +34,16 @@ namespace vp {
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 64;
-constexpr int kThreads = 256;
-constexpr int kWM = 128;           // wave tile rows
-constexpr int kWN = 128;           // wave tile cols
-constexpr int kTM = kWM / 16;      // MFMA tiles per wave along M
-constexpr int kTN = kWN / 16;      // MFMA tiles per wave along N
+constexpr int kWavesM = 2;                  // wave grid of a workgroup
+constexpr int kWavesN = 4;
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWM = kBM / kWavesM;          // wave tile rows
+constexpr int kWN = kBN / kWavesN;          // wave tile cols
+constexpr int kTM = kWM / 16;               // MFMA tiles per wave along M
+constexpr int kTN = kWN / 16;               // MFMA tiles per wave along N
+constexpr int kGA = kBM / 8 / kWaves;       // 8-row groups of A each wave loads per K step
+constexpr int kGB = kBN / 8 / kWaves;       // ... and of B
 constexpr int kGroupM = 8;         // tiles per raster group along M
 // s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8])
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -95,12 +100,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand
     const int m0 = tm * kBM, n0 = tn * kBN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % kWavesM, wn = wave / kWavesM;
 
     // Global -> LDS map (buffer loads straight into LDS, 16 bytes per lane).  One wave
     // instruction fills 8 rows x 128 B = 1 KiB of LDS in lane order: lane L lands on
     // row L/8, physical chunk L%8, so it fetches the logical chunk (L%8) ^ (row & 7).
-    // Wave w fills row groups 8w .. 8w+7 of A and of B (rows 64w .. 64w+63).
+    // Wave w fills 8-row groups w*kGA .. (w+1)*kGA-1 of A and w*kGB .. of B.
     // The buffer resource starts at the tile's first row and ends at the tensor's
     // end, so rows past M (or N) fall outside it and read as zeros.
     const int lrow = lane >> 3;
@@ -111,9 +116,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand
     const uint32_t a_bytes = (uint32_t)((int64_t)(A.rows - m0) * A.ld * 2);
     const uint32_t b_bytes = (uint32_t)((int64_t)(B.rows - n0) * B.ld * 2);
     const uint32_t a_row8 = (uint32_t)(8 * A.ld * 2), b_row8 = (uint32_t)(8 * B.ld * 2);
-    const uint32_t a_off0 = (uint32_t)(((wave * 64 + lrow) * A.ld + lchunk * 8) * 2);
-    const uint32_t b_off0 = (uint32_t)(((wave * 64 + lrow) * B.ld + lchunk * 8) * 2);
-    const int grp = wave * 8 * 8 * kBK;   // LDS element offset of this wave's first row group
+    const uint32_t a_off0 = (uint32_t)(((wave * kGA * 8 + lrow) * A.ld + lchunk * 8) * 2);
+    const uint32_t b_off0 = (uint32_t)(((wave * kGB * 8 + lrow) * B.ld + lchunk * 8) * 2);
+    const int grp_a = wave * kGA * 8 * kBK;   // LDS element offsets of this wave's first groups
+    const int grp_b = kBM * kBK + wave * kGB * 8 * kBK;
 
     // Branch-free: a chunk at or past K (the last partial K step, or a step past the
     // end) gets an offset outside the resource, which reads as zeros.
@@ -126,12 +132,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand
         const uint32_t oa = ok ? a_off0 : kOutOfRange;
         const uint32_t ob = ok ? b_off0 : kOutOfRange;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(buf + grp + i * 8 * kBK), 16,
+        for (int i = 0; i < kGA; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(buf + grp_a + i * 8 * kBK), 16,
                                                      oa + i * a_row8, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_void *)(buf + kBM * kBK + grp + i * 8 * kBK), 16, ob + i * b_row8, 0, 0, 0);
-        }
+#pragma unroll
+        for (int i = 0; i < kGB; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(buf + grp_b + i * 8 * kBK), 16,
+                                                     ob + i * b_row8, 0, 0, 0);
     };
 
     // fragment map: lane reads row (lane & 15) of each 16-row tile, logical chunk kk*4 + lane/16
@@ -163,6 +170,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand
     };
 
     const int KT = (int)ceil_div(K, kBK);
+    constexpr int kReads = kTM + kTN;    // LDS fragment reads per half K step
+    constexpr int kMfmas = kTM * kTN;    // MFMAs per half K step
+    static_assert(kMfmas >= 2 * kReads && kMfmas >= kGA + kGB + kReads, "schedule shape");
     Frags f0, f1;
 
     load_tile(smem, 0);
@@ -177,33 +187,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand
     for (int kt = 0; kt < KT; ++kt) {
         uint16_t *cur = smem + (kt & 1) * kStage;
         uint16_t *nxt = smem + ((kt + 1) & 1) * kStage;
-        // phase 1: F0's 64 MFMAs, with F1's 16 LDS reads spread over the first 32
+        // phase 1: F0's MFMAs, with F1's LDS reads spread over the first of them
         read_frags(cur, ch1, f1);
         mma(f0, 0, kTM);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < kReads; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - 2 * kReads, 0);
         __builtin_amdgcn_sched_barrier(0);
         // every wave has its F1 (nobody reads `cur` any more) and tile kt+1 has landed;
         // no branch: past the last step the loads read zeros and F0 is unused
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        // phase 2: F1's 64 MFMAs, with tile kt+2's 16 loads and the next F0's 16 reads
+        // phase 2: F1's MFMAs, with tile kt+2's loads and the next F0's reads
         load_tile(cur, (kt + 2) * kBK);
         read_frags(nxt, ch0, f0);
         mma(f1, 0, kTM);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < kGA + kGB; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < kReads; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kGA - kGB - kReads, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 

@@ -17,9 +17,9 @@ struct FwdWorkspace {
 };
 FwdWorkspace fwd_workspace(int64_t n, int64_t vs);
 
-// backward workspace: X^T [H, N8], W^T [H, Vs8], dz [N, Vs8], dz^T [Vs, N8] (bf16)
+// backward workspace: X^T [H, N64], W^T [H, Vs64], dz [N, Vs64], dz^T [Vs, N64] (bf16);
 struct BwdWorkspace {
-    int64_t n8, vs8;
+    int64_t n_ld, vs_ld;   // padded leading dimensions (multiples of 64)
     size_t off_xt, off_wt, off_dz, off_dzt;
     size_t bytes;
 };
