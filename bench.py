@@ -81,6 +81,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8192)
     ap.add_argument("--no-embed-bench", action="store_true")
+    ap.add_argument("--no-yardsticks", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -128,25 +129,23 @@ def main():
         a, b = ranges[t]
         vp.vp_lmhead_ce_fwd(x_d, w_full[a:b], y_d, a, b, m[t], s[t], zy[t], workspace=ws_f)
 
-    ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for k in ("embed", "fwd", "combine", "bwd")}
+    calls = ("embed", "fwd", "combine", "bwd")
 
-    def step(record=None):
-        def mark(k, i):
-            if record is not None:
-                record[k][i].record(stream)
-        mark("embed", 0)
+    def step(marks=None):
+        """One step; with `marks`, an event is recorded on the launch stream before each
+        call and after the last one (5 events)."""
+        def mark(i):
+            if marks is not None:
+                marks[i].record(stream)
+        mark(0)
         vp.vp_embed_fwd(ids_d, w0, 0, Vs, out=emb)
-        mark("embed", 1)
-        mark("fwd", 0)
+        mark(1)
         vp.vp_lmhead_ce_fwd(x_d, w0, y_d, 0, Vs, m[0], s[0], zy[0], workspace=ws_f)
-        mark("fwd", 1)
-        mark("combine", 0)
+        mark(2)
         vp.vp_ce_combine(m, s, zy, y_d, loss=loss, lse=lse, loss_mean=mean)
-        mark("combine", 1)
-        mark("bwd", 0)
+        mark(3)
         vp.vp_lmhead_ce_bwd(x_d, w0, y_d, lse, 0, Vs, grad_scale, dx=dx, dw=dw, workspace=ws_b)
-        mark("bwd", 1)
+        mark(4)
 
     # parity gate: no number is reported unless the loss matches the oracle
     step()
@@ -169,25 +168,20 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps, bracketed by synchronisation
+    # timed region: K whole steps, bracketed by synchronisation; the per-call HIP events
+    # are recorded on the launch stream inside the same steps
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        step(marks[k])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
-
-    # per-call durations with events on the same stream (separate pass, same work)
-    per = {k: [] for k in ev}
-    for _ in range(args.steps):
-        step(ev)
-        torch.cuda.synchronize()
-        for k, (a, b) in ev.items():
-            per[k].append(a.elapsed_time(b))
-    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    avg = {c: float(np.mean([mk[i].elapsed_time(mk[i + 1]) for mk in marks]))
+           for i, c in enumerate(calls)}
     ce_ms = avg["fwd"] + avg["combine"] + avg["bwd"]
     alg_flops = 6.0 * N * Vs * H
     achieved = alg_flops / (ce_ms * 1e-3) / 1e12
@@ -202,11 +196,15 @@ def main():
         "ce_executed_tflops": exec_tflops,
         "ce_executed_frac": exec_tflops / PEAK_BF16_TFLOPS,
         "embed_GBs": embed_bytes / (avg["embed"] * 1e-3) / 1e9,
+        # combine: read the [T, N] triples and targets, write loss and lse, mean pass
+        "combine_GBs": (12 * T * N + 8 * N + 8 * N + 12 * N) / (avg["combine"] * 1e-3) / 1e9,
     }
 
     extra = {}
     if not args.no_embed_bench:
         extra["embedding_heavy_lookup"] = embed_bench(torch, vp, vp_inputs, dev, stream, args)
+    if not args.no_yardsticks:
+        extra["yardsticks"] = yardsticks(torch, dev, stream, N, H, Vs)
 
     result = {
         "metric": METRIC,
@@ -241,6 +239,42 @@ def main():
     print(json.dumps(result))
 
 
+def yardsticks(torch, dev, stream, N, H, Vs, reps=10):
+    """Measured ceilings on this machine, for context: the vendor GEMM (torch.matmul on
+    hipBLASLt, bf16) at the three GEMM shapes of the step, and streaming copy / fill."""
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn(N, H, device=dev, generator=g).to(torch.bfloat16)
+    w = torch.randn(Vs, H, device=dev, generator=g).to(torch.bfloat16)
+    dz = torch.randn(N, Vs, device=dev, generator=g).to(torch.bfloat16)
+    dzt = dz.t().contiguous()
+    out = {}
+    fl = 2.0 * N * Vs * H
+    for name, fn in (("matmul_fwd_XWt", lambda: torch.matmul(x, w.t())),
+                     ("matmul_dX_dzW", lambda: torch.matmul(dz, w)),
+                     ("matmul_dW_dztX", lambda: torch.matmul(dzt, x))):
+        ms = timed(fn)
+        out[name + "_tflops"] = fl / (ms * 1e-3) / 1e12
+    del x, w, dz, dzt
+    a = torch.empty(512 * 2**20, dtype=torch.int16, device=dev)   # 1 GiB
+    b = torch.empty_like(a)
+    ms = timed(lambda: b.copy_(a))
+    out["copy_GBs"] = 2 * a.numel() * 2 / (ms * 1e-3) / 1e9
+    ms = timed(lambda: a.fill_(1))
+    out["fill_GBs"] = a.numel() * 2 / (ms * 1e-3) / 1e9
+    return out
+
+
 def embed_bench(torch, vp, vp_inputs, dev, stream, args):
     """The embedding-heavy lookup: 65536 Zipf(1.0) ids on shard 0 ([64000, 4096] bf16) of
     V = 256000, T = 4; algorithmic HBM bytes = output + distinct on-shard rows + ids."""
@@ -265,10 +299,13 @@ def embed_bench(torch, vp, vp_inputs, dev, stream, args):
     o = (ids[rows] >= 0) & (ids[rows] < Vs_e)
     want[o] = w_bits[ids[rows][o]]
     ok = bool(np.array_equal(got, want))
-    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
     times = []
     for i in range(args.warmup + args.steps):
-        flush.fill_(float(i))          # evict L2 / MALL between repetitions
+        # evict L2 / MALL between repetitions with a read-only pass (a write pass would
+        # leave dirty lines draining to HBM during the timed lookup)
+        flush.sum()
+        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         vp.vp_embed_fwd(ids_d, w_d, 0, Vs_e, out=out)
