@@ -18,8 +18,12 @@ before the timed region.  Prints one JSON line (rank 0, N = 1).
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,8 +37,94 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "tokens/sec fused LM-head+vocab-parallel CE fwd+bwd; % bf16 MFMA peak"
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_ce_step_shard_8b.txt")
+COPY_BYTES = 2**30          # the yardsticks' device copy: 1 GiB read + 1 GiB written
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of everything that decides the kernels' code: sources and build flags."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "vocab_lm_head_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "vocab_lm_head_amd", "build.py"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per CE launch from the committed counter summary, if the kernels are
+    still the ones it was measured on; else None."""
+    try:
+        txt = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    h = re.search(r"^kernel_source_hash: (\w+)", txt, re.M)
+    b = re.search(r"^traffic_bytes_per_launch: (\d+)", txt, re.M)
+    if not h or not b or h.group(1) != kernel_source_hash():
+        return None
+    return int(b.group(1))
+
+
+CE_KERNELS = ("CeStatsEpilogue", "merge_slices_kernel", "combine_kernel", "mean_kernel",
+              "transpose_bf16_kernel", "DlogitsEpilogue", "StoreTransposedEpilogue")
+
+
+def _pmc_rows(path, counter):
+    """[(dispatch id, short kernel name, value)] of one counter, summed over its dimensions."""
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = int(r["Dispatch_Id"])
+        n = r["Kernel_Name"]
+        m = re.search(r"namespace\)::(\w+)", n)
+        short = m.group(1) if m else n.split("(")[0]
+        acc.setdefault(k, [short, 0.0])[1] += float(r["Counter_Value"])
+    return sorted((k, v[0], v[1]) for k, v in acc.items())
+
+
+def reduce_pmc(fetch_csv, write_csv, cmd_fetch, cmd_write):
+    """Summarise two counter runs of this script into TRAFFIC_PROFILE: the last step's CE
+    kernels' FETCH_SIZE and WRITE_SIZE (KiB), each scaled by the same counter's reading
+    for the 1 GiB device copy of known size."""
+    out = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows(path, name)
+        copies = [v for _, k, v in rows if "copyBuffer" in k and v > 0.5 * COPY_BYTES / 1024]
+        factor = (COPY_BYTES / 1024) / (sum(copies) / len(copies))
+        last = max(i for i, (_, k, _) in enumerate(rows) if k == "CeStatsEpilogue")
+        step = []
+        for _, k, v in rows[last:]:
+            if k == "embed_kernel" or k not in CE_KERNELS:
+                break
+            step.append((k, v))
+        out[name] = (factor, step, len(copies))
+    f_fetch, step_f, nf = out["FETCH_SIZE"]
+    f_write, step_w, nw = out["WRITE_SIZE"]
+    total = sum(v for _, v in step_f) * f_fetch * 1024 + sum(v for _, v in step_w) * f_write * 1024
+    lines = ["# HBM traffic of one fused CE launch (vp_lmhead_ce_fwd + vp_ce_combine + vp_lmhead_ce_bwd)",
+             "# at the 8B-class shard (N=8192, H=4096, shard [16032, 4096]), from rocprofv3 counters.",
+             "# commands (from the repository root):",
+             f"#   {cmd_fetch}", f"#   {cmd_write}",
+             "#   python3 bench.py --reduce-pmc <fetch csv> <write csv>   (writes this file)",
+             "# Each counter is scaled by its reading for the 1 GiB device copy of the yardsticks",
+             "# (known: 1048576 KiB read and 1048576 KiB written).",
+             f"kernel_source_hash: {kernel_source_hash()}",
+             f"copy_calibration: FETCH factor {f_fetch:.4f} ({nf} copies), WRITE factor {f_write:.4f} ({nw} copies)",
+             "", "kernel                      FETCH_KiB    WRITE_KiB   (raw counter, last step)"]
+    for (k, vf), (_, vw) in zip(step_f, step_w):
+        lines.append(f"{k:26s} {vf:12.0f} {vw:12.0f}")
+    lines += ["", f"traffic_bytes_per_launch: {int(round(total))}",
+              f"traffic_GB_per_launch: {total / 1e9:.4f}"]
+    with open(TRAFFIC_PROFILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def dev_bf16(torch, bits, dev):
@@ -82,7 +172,16 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=8192)
     ap.add_argument("--no-embed-bench", action="store_true")
     ap.add_argument("--no-yardsticks", action="store_true")
+    ap.add_argument("--reduce-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script into profiles/ and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.reduce_pmc:
+        base = "rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{d} -o run -- " \
+               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-embed-bench"
+        reduce_pmc(args.reduce_pmc[0], args.reduce_pmc[1], base.format(c="FETCH_SIZE", d="fetch"),
+                   base.format(c="WRITE_SIZE", d="write"))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(vocab shards would map one per GPU; see DESIGN.md). Run with --gpus 1.",
@@ -227,7 +326,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "fused LM-head CE fwd+combine+bwd (vp_lmhead_ce_fwd + "
                      "vp_ce_combine + vp_lmhead_ce_bwd)", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None, "algorithmic_flops_per_launch": alg_flops,
+                     "traffic": recorded_traffic(), "algorithmic_flops_per_launch": alg_flops,
                      "avg_launch_ms": ce_ms},
         "breakdown": breakdown,
         "parity": parity,
