@@ -44,7 +44,8 @@ extern "C" {
 typedef enum {
     VP_OK = 0,
     VP_ERR_NULL = -1,       /* a required pointer is null                      */
-    VP_ERR_SHAPE = -2,      /* a size is negative / zero where it must not be, or V % T != 0 */
+    VP_ERR_SHAPE = -2,      /* a size is negative / zero where it must not be, too large
+                               (n, h or Vs above 2^20 in the CE calls), or V % T != 0 */
     VP_ERR_RANGE = -3,      /* vocab_end <= vocab_start, or t outside [0, T)    */
     VP_ERR_ALIGN = -4,      /* H % 8 != 0 or a pointer is misaligned           */
     VP_ERR_WORKSPACE = -5,  /* workspace pointer null or smaller than required */

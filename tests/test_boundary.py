@@ -145,6 +145,9 @@ def test_bwd_validation_and_workspace(lib):
     assert call(dx=FAKE + 8) == ALIGN
     assert call(h=8, hi=0) == RANGE
     assert call(n=-1) == SHAPE
+    assert call(h=(1 << 20) + 8) == SHAPE      # rows above 2^20 elements
+    assert call(hi=(1 << 20) + 1) == SHAPE
+    assert call(n=(1 << 20) + 1) == SHAPE
 
 
 def test_product_package_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -47,7 +47,7 @@ class VPError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it first with `python -m vocab_lm_head_amd.build` "
+            f"{LIB_PATH} is missing: build it first with `python vocab_lm_head_amd/build.py` "
             "(the HIP library is required; there is no CPU fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():

@@ -1,6 +1,8 @@
 """Build ``libvplmhead.so`` (HIP C++ for gfx950) in-tree with hipcc.
 
-    python -m vocab_lm_head_amd.build          # compile every source, link the library
+    python vocab_lm_head_amd/build.py          # compile every source, link the library
+
+(Run it by path: importing the package loads the library this script builds.)
 
 Objects go to ``_build/`` at the repository root; the shared library is
 written next to this file so that the Python binding finds it.

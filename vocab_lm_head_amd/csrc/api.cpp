@@ -17,8 +17,9 @@ inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)
 int check_shard(int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end) {
     if (n < 0 || h <= 0) return VP_ERR_SHAPE;
     if (vocab_start < 0 || vocab_end <= vocab_start) return VP_ERR_RANGE;
-    // the GEMM tiling indexes rows and columns with 32-bit integers
-    if (n > INT32_MAX / 2 || h > INT32_MAX / 2 || vocab_end - vocab_start > INT32_MAX / 2)
+    // the GEMMs address 256-row operand panels through 1 GiB buffer resources, and
+    // every operand row (H, N or Vs elements, padded) must stay below 2M elements
+    if (n > (1 << 20) || h > (1 << 20) || vocab_end - vocab_start > (1 << 20))
         return VP_ERR_SHAPE;
     if (h % 8 != 0) return VP_ERR_ALIGN;
     return VP_OK;

@@ -78,8 +78,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // dword 3 of a gfx9 raw buffer resource (32-bit data format; no swizzle, no index)
 constexpr int kBufferFlags = 0x00020000;
-// a buffer offset past any resource this kernel builds (they stay below 2 GiB)
+// resources are capped at 1 GiB (no K step of a 256-row panel reaches further when
+// its rows are shorter than 2M elements); this offset is past all of them
+constexpr uint32_t kResourceCap = 1u << 30;
 constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ uint32_t resource_bytes(int64_t b) {
+    return b <= 0 ? 0u : (b >= (int64_t)kResourceCap ? kResourceCap : (uint32_t)b);
+}
 
 // One K step of operand fragments held by a wave: 8 A rows-blocks and 8 B col-blocks.
 struct Frags {
@@ -113,8 +119,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand
     const char *a_panel = (const char *)(A.p + (int64_t)m0 * A.ld);
     const char *b_panel = (const char *)(B.p + (int64_t)n0 * B.ld);
     // bytes from the panel start to the end of the last row (past it: zeros)
-    const uint32_t a_bytes = (uint32_t)((int64_t)(A.rows - m0) * A.ld * 2);
-    const uint32_t b_bytes = (uint32_t)((int64_t)(B.rows - n0) * B.ld * 2);
+    const uint32_t a_bytes = resource_bytes((int64_t)(A.rows - m0) * A.ld * 2);
+    const uint32_t b_bytes = resource_bytes((int64_t)(B.rows - n0) * B.ld * 2);
     const uint32_t a_row8 = (uint32_t)(8 * A.ld * 2), b_row8 = (uint32_t)(8 * B.ld * 2);
     const uint32_t a_off0 = (uint32_t)(((wave * kGA * 8 + lrow) * A.ld + lchunk * 8) * 2);
     const uint32_t b_off0 = (uint32_t)(((wave * kGB * 8 + lrow) * B.ld + lchunk * 8) * 2);
