@@ -114,7 +114,7 @@ int vp_lmhead_ce_fwd(const uint16_t *hidden, const uint16_t *w_shard, const int6
  *   loss_mean[0] = sum_i loss[i] / max(1, #{i : targets[i] != ignore_index})
  *   m, s, zy  fp32 [T, n] row-major (row r = shard r's vp_lmhead_ce_fwd output)
  *   targets   int64 [n];  loss, lse fp32 [n];  loss_mean fp32 [1]; all overwritten
- * n == 0: writes loss_mean = 0 only.  Errors: NULL, SHAPE (n < 0, T < 1), ALIGN, HIP.
+ * n == 0: writes loss_mean = 0 only.  Errors: NULL, SHAPE (n < 0, n > 2^31, T < 1), ALIGN, HIP.
  */
 int vp_ce_combine(const float *m, const float *s, const float *zy,
                   const int64_t *targets, int64_t n, int32_t T, int64_t ignore_index,

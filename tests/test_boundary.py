@@ -122,6 +122,7 @@ def test_combine_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 16, 2, -100, FAKE, FAKE, None, None) == NULL
     assert f(None, FAKE, FAKE, FAKE, 16, 2, -100, FAKE, FAKE, FAKE, None) == NULL
     assert f(FAKE, FAKE, FAKE, FAKE + 4, 16, 2, -100, FAKE, FAKE, FAKE, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, (1 << 31) + 1, 2, -100, FAKE, FAKE, FAKE, None) == SHAPE
 
 
 def test_bwd_validation_and_workspace(lib):

@@ -91,7 +91,8 @@ int vp_lmhead_ce_fwd(const uint16_t *hidden, const uint16_t *w_shard, const int6
 int vp_ce_combine(const float *m, const float *s, const float *zy, const int64_t *targets,
                   int64_t n, int32_t T, int64_t ignore_index, float *loss, float *lse,
                   float *loss_mean, hipStream_t stream) {
-    if (n < 0 || T < 1 || n > INT64_MAX / T) return VP_ERR_SHAPE;
+    // one thread per token: n is capped so that the grid stays far inside its limits
+    if (n < 0 || T < 1 || n > ((int64_t)1 << 31) || n > INT64_MAX / T) return VP_ERR_SHAPE;
     if (!loss_mean) return VP_ERR_NULL;
     if (n > 0) {
         if (!m || !s || !zy || !targets || !loss || !lse) return VP_ERR_NULL;

@@ -108,18 +108,24 @@ struct DlogitsEpilogue {
     __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane, int m0,
                                                int n0, uint16_t *lds) const {
         const int rsub = 4 * (lane >> 4);
+        // the lane's targets and lse values, all loaded before any is used (one memory
+        // latency per tile); columns past N read token N-1 and are masked below
+        int64_t tg[kTN];
+        float ls[kTN];
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int nc = min(nbase + 16 * j + (lane & 15), N - 1);
+            tg[j] = targets[nc];
+            ls[j] = lse[nc];
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
             const int n = nbase + 16 * j + (lane & 15);
             const bool ncol = n < N;
-            float g = 0.f, lsel = 0.f;
-            int64_t trow = -1;
-            if (ncol) {
-                const int64_t y = targets[n];
-                g = (y == ignore_index) ? 0.f : grad_scale;
-                lsel = lse[n] * kLog2e;
-                trow = y - start;
-            }
+            const float g = (tg[j] == ignore_index) ? 0.f : grad_scale;
+            const float lsel = ls[j] * kLog2e;
+            const int64_t trow = tg[j] - start;
 #pragma unroll
             for (int i = 0; i < kTM; ++i) {
                 const int row0 = mbase + 16 * i + rsub;   // vocabulary row of r = 0
@@ -135,56 +141,77 @@ struct DlogitsEpilogue {
         }
         __syncthreads();
         const int t = threadIdx.x;
-        // token-major: 256 rows x 32 chunks of 16 B; a wave covers two rows per instruction
-#pragma unroll 4
-        for (int it = 0; it < (kBN * kBM / 8) / kThreads; ++it) {
-            const int q = it * kThreads + t;
-            const int r = q >> 5, c = (q & 31) * 8;
-            const int n = n0 + r;
-            if (n < N && m0 + c < ld_dz)
-                *(u32x4 *)(dz + (int64_t)n * ld_dz + m0 + c) = *(const u32x4 *)(lds + dz_swz(r, c));
+        // Both passes read all of their LDS chunks first, then issue their stores; rows
+        // past N (or M) lie outside the store resource and are dropped by the hardware,
+        // padding columns past the leading dimension get an offset outside it.
+        {   // token-major: thread t owns 16-byte chunk t % 32 of rows t/32 + 16 it
+            const int c = t & 31, r0 = t >> 5;
+            constexpr int kIt = (kBN * kBM / 8) / kThreads;
+            constexpr int kRowStep = kThreads / 32;
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(dz + (int64_t)n0 * ld_dz + m0, ((int64_t)(N - n0) * ld_dz - m0) * 2);
+            const bool colok = m0 + 8 * c < ld_dz;
+            u32x4 v[kIt];
+#pragma unroll
+            for (int it = 0; it < kIt; ++it)
+                v[it] = *(const u32x4 *)(lds + dz_swz(r0 + kRowStep * it, 8 * c));
+#pragma unroll
+            for (int it = 0; it < kIt; ++it)
+                store16<kStoreNT>(v[it], rs,
+                        colok ? (uint32_t)(((int64_t)(r0 + kRowStep * it) * ld_dz + 8 * c) * 2) : kOutOfRange);
         }
-        // vocab-major: a lane gathers 4 vocab rows x 8 tokens (eight 8-byte LDS reads) and
-        // writes four 16-byte chunks; 32 lanes cover 512 contiguous bytes of each row
-#pragma unroll 2
-        for (int it = 0; it < (kBM * kBN / 32) / kThreads; ++it) {
-            const int q = it * kThreads + t;
-            const int v0 = (q >> 5) * 4, c = (q & 31) * 8;   // first vocab row, first token
-            if (n0 + c >= ld_dzt || m0 + v0 >= M) continue;
-            u32x2 rd[8];
+        {   // vocab-major: a lane gathers 4 vocab rows x 8 tokens (eight 8-byte LDS reads)
+            // per iteration and writes four 16-byte chunks; 32 lanes cover a 512-byte row
+            const int c = (t & 31) * 8, vq = (t >> 5) * 4;
+            constexpr int kIt = (kBM * kBN / 32) / kThreads;
+            constexpr int kVocabStep = 4 * kThreads / 32;
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(dzt + (int64_t)m0 * ld_dzt + n0, ((int64_t)(M - m0) * ld_dzt - n0) * 2);
+            const bool colok = n0 + c < ld_dzt;
+            u32x2 rd[kIt][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) rd[e] = *(const u32x2 *)(lds + dz_swz(c + e, v0));
+            for (int it = 0; it < kIt; ++it)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                if (m0 + v0 + v >= M) break;
-                const int w = v >> 1, sh = (v & 1) * 16;
-                u32x4 o;
+                for (int e = 0; e < 8; ++e)
+                    rd[it][e] = *(const u32x2 *)(lds + dz_swz(c + e, vq + kVocabStep * it));
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    o[p] = ((rd[2 * p][w] >> sh) & 0xFFFFu) | (((rd[2 * p + 1][w] >> sh) & 0xFFFFu) << 16);
-                *(u32x4 *)(dzt + (int64_t)(m0 + v0 + v) * ld_dzt + n0 + c) = o;
-            }
+            for (int it = 0; it < kIt; ++it)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int w = v >> 1, sh = (v & 1) * 16;
+                    u32x4 o;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        o[p] = ((rd[it][2 * p][w] >> sh) & 0xFFFFu) |
+                               (((rd[it][2 * p + 1][w] >> sh) & 0xFFFFu) << 16);
+                    const int64_t row = vq + kVocabStep * it + v;
+                    store16<kStoreNT>(o, rs, colok ? (uint32_t)((row * ld_dzt + c) * 2) : kOutOfRange);
+                }
         }
     }
 };
 
-// out[n, m] = C[m, n] (fp32), m < M, n < N; M a multiple of 4.
+// out[n, m] = C[m, n] (fp32), m < M, n < N; M a multiple of 4.  Stores go through a
+// resource over the output rows from the workgroup's first one: rows past N are
+// outside it, columns past M get an offset outside it.
 struct StoreTransposedEpilogue {
     float *out;
     int64_t ldo;
     int M, N;
 
-    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane, int, int,
-                                               uint16_t *) const {
+    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane, int m0,
+                                               int n0, uint16_t *) const {
         const int rsub = 4 * (lane >> 4);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(out + (int64_t)n0 * ldo + m0, ((int64_t)(N - n0) * ldo - m0) * 4);
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
-            const int n = nbase + 16 * j + (lane & 15);
-            if (n >= N) continue;
+            const int64_t nl = nbase - n0 + 16 * j + (lane & 15);
 #pragma unroll
             for (int i = 0; i < kTM; ++i) {
-                const int m = mbase + 16 * i + rsub;
-                if (m < M) *(f32x4 *)(out + (int64_t)n * ldo + m) = acc[i][j];
+                const int ml = mbase - m0 + 16 * i + rsub;
+                store16<kStoreDefault>(__builtin_bit_cast(u32x4, acc[i][j]), rs,
+                        m0 + ml < M ? (uint32_t)((nl * ldo + ml) * 4) : kOutOfRange);
             }
         }
     }

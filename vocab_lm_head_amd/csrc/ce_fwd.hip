@@ -28,75 +28,117 @@ struct CeStatsEpilogue {
     __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane, int, int,
                                                uint16_t *) const {
         if (mbase >= M) return;                   // wave tile entirely past the shard
-        const bool full = mbase + kWM <= M;
         const int rsub = 4 * (lane >> 4);
         const int64_t p = mbase / kSlice;
         float *pm = part + p * N;
         float *ps = part + (slices + p) * N;
         float *pz = part + (2 * slices + p) * N;
+        // all of this lane's targets are loaded before any is used: one memory latency
+        // per tile; columns past N read token N-1 and are not stored
+        int64_t tg[kTN];
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) tg[j] = targets[min(nbase + 16 * j + (lane & 15), N - 1)];
+        __builtin_amdgcn_sched_barrier(0);
+        // rows past the shard's end (only in its last tile; a wave-uniform branch)
+        // hold no shard data: -inf drops them from the max and the sum
+        if (mbase + kWM > M) {
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (mbase + 16 * i + rsub + r >= M)
+#pragma unroll
+                        for (int j = 0; j < kTN; ++j) acc[i][j][r] = -INFINITY;
+        }
+        // per column: the lane's 32 rows, then the 4 lanes sharing the column
+        float mx[kTN];
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
-            const int n = nbase + 16 * j + (lane & 15);
-            // target row relative to this wave tile; -1 unless the target lies in the shard
-            // (rows past the shard's end exist in the last tile but hold no shard data)
-            int64_t trow = -1;
-            if (n < N) {
-                const int64_t local = targets[n] - start;
-                if (local >= 0 && local < M) trow = local - mbase;
-            }
-            float mx = -INFINITY;
+            float a = acc[0][j][0];
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a = fmaxf(a, acc[i][j][r]);
+            mx[j] = a;
+        }
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 16));
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 32));
+        float sum[kTN], zy[kTN];
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            // target row relative to this lane's first row; matches 16 i + r for at most
+            // one (i, r), and never when the target lies outside the shard
+            const int64_t local = tg[j] - start;
+            const int tr = (local >= 0 && local < M) ? (int)(local - mbase) - rsub : -1;
+            const float mxl = mx[j] * kLog2e;
+            float sj = 0.f, zj = 0.f;
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * i + rsub + r;
-                    if (full || mbase + row < M) mx = fmaxf(mx, acc[i][j][r]);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mxl = mx * kLog2e;
-            float s = 0.f, zy = 0.f;
-#pragma unroll
-            for (int i = 0; i < kTM; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * i + rsub + r;
                     const float v = acc[i][j][r];
-                    if (full || mbase + row < M) s += fast_exp2(fmaf(v, kLog2e, -mxl));
-                    if (row == trow) zy = v;
+                    sj += fast_exp2(fmaf(v, kLog2e, -mxl));
+                    zj = (tr == 16 * i + r) ? v : zj;
                 }
-            s += __shfl_xor(s, 16);
-            s += __shfl_xor(s, 32);
-            zy += __shfl_xor(zy, 16);
-            zy += __shfl_xor(zy, 32);
-            if (lane < 16 && n < N) {
-                pm[n] = mx;
-                ps[n] = s;
-                pz[n] = zy;
+            sum[j] = sj;
+            zy[j] = zj;
+        }
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            sum[j] += __shfl_xor(sum[j], 16);
+            zy[j] += __shfl_xor(zy[j], 16);
+        }
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            sum[j] += __shfl_xor(sum[j], 32);
+            zy[j] += __shfl_xor(zy[j], 32);
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) {
+                const int n = nbase + 16 * j + lane;
+                if (n < N) {
+                    pm[n] = mx[j];
+                    ps[n] = sum[j];
+                    pz[n] = zy[j];
+                }
             }
         }
     }
 };
 
 // Merge the shard's per-slice partials of each token.  A workgroup takes 32
-// tokens; its 8 thread groups each merge every 8th slice (independent loads
-// in flight), then the 8 partial results are merged through LDS.
-constexpr int kMergeTok = 32, kMergeGrp = 8;
+// tokens; its 8 thread groups each merge every 8th slice, kMergeBatch slices at a
+// time with all of their loads issued before the first is used, then the 8
+// partial results are merged through LDS.
+constexpr int kMergeTok = 32, kMergeGrp = 8, kMergeBatch = 4;
 __global__ __launch_bounds__(kMergeTok * kMergeGrp) void merge_slices_kernel(
     const float *__restrict__ part, int64_t slices, int64_t n, float *__restrict__ m_out,
     float *__restrict__ s_out, float *__restrict__ zy_out) {
     __shared__ float sm[kMergeGrp][kMergeTok], ss[kMergeGrp][kMergeTok], sz[kMergeGrp][kMergeTok];
     const int t = threadIdx.x % kMergeTok, g = threadIdx.x / kMergeTok;
     const int64_t i = (int64_t)blockIdx.x * kMergeTok + t;
+    const int64_t ic = i < n ? i : n - 1;   // past n: a valid address, result unused
     float m = -INFINITY, s = 0.f, zy = 0.f;
-    if (i < n) {
-        for (int64_t p = g; p < slices; p += kMergeGrp) {
-            const float mp = part[p * n + i];
-            const float sp = part[(slices + p) * n + i];
-            zy += part[(2 * slices + p) * n + i];
-            const float mx = fmaxf(m, mp);
-            s = s * fast_exp2((m - mx) * kLog2e) + sp * fast_exp2((mp - mx) * kLog2e);
+    for (int64_t p0 = g; p0 < slices; p0 += kMergeGrp * kMergeBatch) {
+        float mp[kMergeBatch], sp[kMergeBatch], zp[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const int64_t p = p0 + u * kMergeGrp;
+            const int64_t pc = p < slices ? p : slices - 1;
+            mp[u] = part[pc * n + ic];
+            sp[u] = part[(slices + pc) * n + ic];
+            zp[u] = part[(2 * slices + pc) * n + ic];
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            if (p0 + u * kMergeGrp >= slices) break;
+            const float mx = fmaxf(m, mp[u]);
+            s = s * fast_exp2((m - mx) * kLog2e) + sp[u] * fast_exp2((mp[u] - mx) * kLog2e);
             m = mx;
+            zy += zp[u];
         }
     }
     sm[g][t] = m;

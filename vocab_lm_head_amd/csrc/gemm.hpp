@@ -87,6 +87,25 @@ __device__ __forceinline__ uint32_t resource_bytes(int64_t b) {
     return b <= 0 ? 0u : (b >= (int64_t)kResourceCap ? kResourceCap : (uint32_t)b);
 }
 
+// A raw buffer resource over `bytes` bytes from `base` (capped as above).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, resource_bytes(bytes), kBufferFlags);
+}
+
+// 16-byte store through a buffer resource: the hardware drops a store whose offset
+// lies outside the resource, so ragged tile edges need no branch.  kPolicy is the
+// instruction's cache-policy field; kStoreNT (bit 1, "nt") marks the data
+// non-temporal.  The backward's dlogits copies (2 x N x Vs bf16, far larger than L2)
+// are stored that way so that they do not evict the operand panels the
+// neighbouring tiles are still reading; measured on the 8B-class shard, nt on
+// the fp32 gradient stores was slightly slower, so those use the default policy.
+constexpr int kStoreNT = 2;
+constexpr int kStoreDefault = 0;
+template <int kPolicy>
+__device__ __forceinline__ void store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolicy);
+}
+
 // One K step of operand fragments held by a wave: 8 A rows-blocks and 8 B col-blocks.
 struct Frags {
     bf16x8 a[kTM];
