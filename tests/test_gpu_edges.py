@@ -106,6 +106,36 @@ def test_targets_on_shard_edges(vp):
     _full_check(vp, xb, wb, y, T=T, label="edge targets")
 
 
+@pytest.mark.parametrize("T", [9, 16, 17, 33])
+def test_combine_many_shards(vp, T):
+    """Combine over more shards than it reads in one batch (8): per-shard statistics
+    of a dense problem (fp32, as the forward hands them over), merged on the GPU,
+    against the dense loss of the same logits; 20% of the targets are ignored."""
+    import torch
+    r = np.random.default_rng(100 + T)
+    N, Vs = 300, 7
+    V = T * Vs
+    z = r.standard_normal((N, V)) * 4.0 + r.standard_normal((1, V)) * 3.0
+    y = r.integers(0, V, N).astype(np.int64)
+    y[r.random(N) < 0.2] = -100
+    stats = [oracle.shard_stats(z[:, t * Vs:(t + 1) * Vs], y, t * Vs) for t in range(T)]
+    m, s, zy = (np.stack([st[k] for st in stats]).astype(np.float32) for k in range(3))
+    loss, lse, mean = oracle.dense_ce(z, y)
+    log(f"  combine T={T}, N={N}")
+    dl, dlse, dmean = vp.vp_ce_combine(torch.from_numpy(m).cuda(), torch.from_numpy(s).cuda(),
+                                       torch.from_numpy(zy).cuda(), dev_i64(y))
+    torch.cuda.synchronize()
+    assert_loss_close(host(dl), loss)
+    assert_loss_close(host(dlse), lse, "lse")
+    assert abs(float(dmean.item()) - mean) <= 2e-3
+
+
+def test_twelve_shards_full_path(vp):
+    """T=12 (V=1200, Vs=100): every shard's forward, combine over 12, backward of three shards."""
+    xb, wb, y = _problem(12, 333, 64, 1200, logit_std=4.0, ignore_frac=0.1)
+    _full_check(vp, xb, wb, y, T=12, bwd_shards=[0, 5, 11], label="T=12")
+
+
 def test_large_logits(vp):
     """Logit std 40: the stabilising maximum matters; sum-exp must not overflow."""
     xb, wb, y = _problem(7, 130, 128, 640, logit_std=40.0)

@@ -112,16 +112,17 @@ struct Frags {
     bf16x8 b[kTN];
 };
 
-template <class Epilogue>
-__global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand B, int K,
-                                                              int tiles_m, int tiles_n,
-                                                              Epilogue epi) {
-    // two LDS stages of one [256 x 64] A tile and one [256 x 64] B tile each (2 x 64 KiB)
-    constexpr int kStage = (kBM + kBN) * kBK;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * kStage];
+// two LDS stages of one [256 x 64] A tile and one [256 x 64] B tile each (2 x 64 KiB)
+constexpr int kStage = (kBM + kBN) * kBK;
 
+// One output tile of C = A B^T: block `bid` of a tiles_m x tiles_n grid, computed by
+// the workgroup's kThreads threads with `smem` (2 kStage elements) as its LDS.
+template <class Epilogue>
+__device__ __forceinline__ void gemm_nt_tile(const Operand &A, const Operand &B, int K,
+                                             int tiles_m, int tiles_n, const Epilogue &epi,
+                                             int bid, uint16_t *smem) {
     int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    tile_of_block(bid, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * kBM, n0 = tn * kBN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -251,9 +252,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand
     __syncthreads();
 
     // accumulator layout of v_mfma_f32_16x16x32: acc[i][j][r] is
-    //   row m0 + wm*128 + 16 i + 4 (lane / 16) + r,  column n0 + wn*128 + 16 j + (lane % 16)
-    // The epilogue may use the 128 KiB of LDS (`smem`); all 256 threads call it.
+    //   row m0 + wm*kWM + 16 i + 4 (lane / 16) + r,  column n0 + wn*kWN + 16 j + (lane % 16)
+    // The epilogue may use the 128 KiB of LDS (`smem`); all kThreads threads call it.
     epi(acc, m0 + wm * kWM, n0 + wn * kWN, lane, m0, n0, smem);
+}
+
+template <class Epilogue>
+__global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand B, int K,
+                                                              int tiles_m, int tiles_n,
+                                                              Epilogue epi) {
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * kStage];
+    gemm_nt_tile(A, B, K, tiles_m, tiles_n, epi, blockIdx.x, smem);
+}
+
+// One GEMM of a grouped launch.
+template <class Epilogue>
+struct GemmJob {
+    Operand A, B;
+    int K, tiles_m, tiles_n;
+    Epilogue epi;
+};
+
+// Two independent GEMMs in one launch: blocks [0, tiles of j0) compute j0's tiles, the
+// rest j1's.  Workgroups that finish j0 go straight on to j1 (no drain between two
+// launches, and j1's last partial round overlaps j0's); put the job with the longer K
+// first.  When j0's tile count is a multiple of 8, j1's blocks keep the XCD mapping.
+template <class Epilogue>
+__global__ __launch_bounds__(kThreads, 1) void gemm_nt_pair_kernel(GemmJob<Epilogue> j0,
+                                                                   GemmJob<Epilogue> j1) {
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * kStage];
+    const int b0 = j0.tiles_m * j0.tiles_n;
+    const bool first = (int)blockIdx.x < b0;
+    const GemmJob<Epilogue> &j = first ? j0 : j1;
+    gemm_nt_tile(j.A, j.B, j.K, j.tiles_m, j.tiles_n, j.epi, first ? (int)blockIdx.x : (int)blockIdx.x - b0,
+                 smem);
 }
 
 // Launch geometry of a GEMM over an M x N output.
