@@ -15,7 +15,6 @@
 //      writes it in bf16 twice, token-major dz [N, Vs64] and vocab-major dz^T [Vs, N64];
 //   3. dX_r^T = W_r^T dz^T  (A = W_r^T [H, Vs64], B = dz [N, Vs64]), K = Vs64
 //   4. dW_r^T = X^T dz      (A = X^T [H, N64],   B = dz^T [Vs, N64]),  K = N64
-//      (3 and 4 share one launch)
 // The [N, Vs] dlogits must reach memory once: a register-only fusion of dX and
 // dW would need fp32 atomics on [tile, H] slabs for every tile, far below the
 // MFMA roofline at H = 4096.
@@ -274,18 +273,19 @@ hipError_t launch_ce_bwd(const uint16_t *x, const uint16_t *w, const int64_t *ta
                            stream, Operand{w, h, (int)vs}, Operand{x, h, (int)n}, (int)h,
                            g.tiles_m, g.tiles_n, epi);
     }
-    {   // one launch for both gradients (dX first: its K = Vs64 is the longer one)
-        //   dX_r^T [H, N] = W_r^T [H, Vs64] . dz [N, Vs64]^T
-        //   dW_r^T [H, Vs] = X^T [H, N64] . dz^T [Vs, N64]^T
-        const GemmGrid gx = gemm_grid(h, n), gw = gemm_grid(h, vs);
-        GemmJob<StoreTransposedEpilogue> jx{Operand{wt, b.vs_ld, (int)h}, Operand{dz, b.vs_ld, (int)n},
-                                            (int)b.vs_ld, gx.tiles_m, gx.tiles_n,
-                                            StoreTransposedEpilogue{dx, h, (int)h, (int)n}};
-        GemmJob<StoreTransposedEpilogue> jw{Operand{xt, b.n_ld, (int)h}, Operand{dzt, b.n_ld, (int)vs},
-                                            (int)b.n_ld, gw.tiles_m, gw.tiles_n,
-                                            StoreTransposedEpilogue{dw, h, (int)h, (int)vs}};
-        hipLaunchKernelGGL(gemm_nt_pair_kernel<StoreTransposedEpilogue>,
-                           dim3(gx.blocks() + gw.blocks()), dim3(kThreads), 0, stream, jx, jw);
+    {   // dX_r^T [H, N] = W_r^T [H, Vs64] . dz [N, Vs64]^T
+        const GemmGrid g = gemm_grid(h, n);
+        StoreTransposedEpilogue epi{dx, h, (int)h, (int)n};
+        hipLaunchKernelGGL(gemm_nt_kernel<StoreTransposedEpilogue>, dim3(g.blocks()), dim3(kThreads),
+                           0, stream, Operand{wt, b.vs_ld, (int)h}, Operand{dz, b.vs_ld, (int)n},
+                           (int)b.vs_ld, g.tiles_m, g.tiles_n, epi);
+    }
+    {   // dW_r^T [H, Vs] = X^T [H, N64] . dz^T [Vs, N64]^T
+        const GemmGrid g = gemm_grid(h, vs);
+        StoreTransposedEpilogue epi{dw, h, (int)h, (int)vs};
+        hipLaunchKernelGGL(gemm_nt_kernel<StoreTransposedEpilogue>, dim3(g.blocks()), dim3(kThreads),
+                           0, stream, Operand{xt, b.n_ld, (int)h}, Operand{dzt, b.n_ld, (int)vs},
+                           (int)b.n_ld, g.tiles_m, g.tiles_n, epi);
     }
     return hipGetLastError();
 }

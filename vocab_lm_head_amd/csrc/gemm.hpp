@@ -265,29 +265,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand
     gemm_nt_tile(A, B, K, tiles_m, tiles_n, epi, blockIdx.x, smem);
 }
 
-// One GEMM of a grouped launch.
-template <class Epilogue>
-struct GemmJob {
-    Operand A, B;
-    int K, tiles_m, tiles_n;
-    Epilogue epi;
-};
-
-// Two independent GEMMs in one launch: blocks [0, tiles of j0) compute j0's tiles, the
-// rest j1's.  Workgroups that finish j0 go straight on to j1 (no drain between two
-// launches, and j1's last partial round overlaps j0's); put the job with the longer K
-// first.  When j0's tile count is a multiple of 8, j1's blocks keep the XCD mapping.
-template <class Epilogue>
-__global__ __launch_bounds__(kThreads, 1) void gemm_nt_pair_kernel(GemmJob<Epilogue> j0,
-                                                                   GemmJob<Epilogue> j1) {
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * kStage];
-    const int b0 = j0.tiles_m * j0.tiles_n;
-    const bool first = (int)blockIdx.x < b0;
-    const GemmJob<Epilogue> &j = first ? j0 : j1;
-    gemm_nt_tile(j.A, j.B, j.K, j.tiles_m, j.tiles_n, j.epi, first ? (int)blockIdx.x : (int)blockIdx.x - b0,
-                 smem);
-}
-
 // Launch geometry of a GEMM over an M x N output.
 struct GemmGrid {
     int tiles_m, tiles_n;
