@@ -52,3 +52,16 @@ def embed_lookup(ids, w_rows, start, end):
         else:
             out.append([0] * H)
     return out
+
+
+def embed_grad(ids, dout_rows, start, end):
+    """Weight gradient of the per-shard lookup: each owned token adds its gradient row
+    to local row id - start (the adjoint of ``embed_lookup``)."""
+    H = len(dout_rows[0])
+    out = [[0.0] * H for _ in range(end - start)]
+    for i, tok_id in enumerate(ids):
+        if start <= tok_id < end:
+            row = out[tok_id - start]
+            for k in range(H):
+                row[k] += dout_rows[i][k]
+    return out

@@ -34,7 +34,8 @@ import numpy as np
 DEFAULT_IGNORE_INDEX = -100
 
 __all__ = [
-    "DEFAULT_IGNORE_INDEX", "shard_range", "embed_shard", "logits",
+    "DEFAULT_IGNORE_INDEX", "shard_range", "embed_shard", "embed_shard_grad",
+    "embed_shard_grad_rows", "logits",
     "shard_stats", "combine_triples", "pages_sharded_ce", "dense_ce",
     "dense_dlogits", "shard_grads", "mean_scale", "lse_dense_chunked",
     "shard_stats_chunked", "dz_rows", "dz_cols",
@@ -70,6 +71,37 @@ def embed_shard(ids, w_shard: np.ndarray, start: int, end: int) -> np.ndarray:
     out = np.zeros((ids.shape[0], w_shard.shape[1]), dtype=w_shard.dtype)
     own = (ids >= start) & (ids < end)
     out[own] = w_shard[ids[own] - start]
+    return out
+
+
+def embed_shard_grad(ids, dout: np.ndarray, start: int, end: int) -> np.ndarray:
+    """Gradient of one shard's masked lookup with respect to its weight rows.
+
+    The lookup of "5 Vocab Parallelism", 5.2.1 is linear in the shard's weight:
+    out = P W_r, where P[i, k] = 1 when token i's id is owned and id - start == k,
+    else 0.  Its adjoint is dW_r = P^T dOut: every owned token adds its output
+    gradient to row id - start, off-shard tokens add nothing, and repeated ids
+    accumulate.  (The pages state the lookup, not this backward; it is the
+    plain adjoint.)  Returns fp64 [end - start, H].
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    g = np.asarray(dout, dtype=np.float64)
+    out = np.zeros((end - start, g.shape[1]))
+    own = (ids >= start) & (ids < end)
+    np.add.at(out, ids[own] - start, g[own])
+    return out
+
+
+def embed_shard_grad_rows(ids, dout: np.ndarray, start: int, rows) -> np.ndarray:
+    """Rows ``rows`` (local indices) of ``embed_shard_grad``, each the fp64 sum of
+    the output gradients of the tokens whose id is start + row."""
+    ids = np.asarray(ids, dtype=np.int64)
+    g = np.asarray(dout)
+    out = np.zeros((len(rows), g.shape[1]))
+    for k, r in enumerate(rows):
+        sel = np.nonzero(ids == start + int(r))[0]
+        if sel.size:
+            out[k] = g[sel].astype(np.float64).sum(axis=0)
     return out
 
 

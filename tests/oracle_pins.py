@@ -5,7 +5,9 @@ on the real oracle (``test_oracle.py``) and on copies of it with a planted
 mistake (``test_oracle_mutations.py``, where at least one pin must fail).
 
 What pins what:
-  * the pages' worked lookup examples (golden JSON, cited inside each file);
+  * the pages' worked lookup examples (golden JSON, cited inside each file),
+    also run backwards through the lookup's weight gradient;
+  * the lookup gradient as the exact adjoint of the lookup (inner products);
   * closed forms of the cross entropy (uniform logits -> log V; a hand-solved
     4-way example) and of its gradient;
   * the identity "sharded statistics merged == dense cross entropy";
@@ -94,6 +96,79 @@ def pin_embed_brute(o):
     inr = (ids >= 0) & (ids < V)
     assert np.array_equal(dense[inr], W[ids[inr]].astype(np.int64))
     assert not dense[~inr].any()
+
+
+def pin_embed_grad_brute(o):
+    """Weight gradient of the lookup against the pure-Python loops (random ids with
+    repeats, off-shard and out-of-range ids)."""
+    from oracle import brute
+    rng = np.random.default_rng(11)
+    V, T, H = 24, 3, 5
+    ids = np.concatenate([rng.integers(-3, V + 3, 60), [0, 7, 8, 15, 16, 23, 8, 8]])
+    g = rng.standard_normal((ids.size, H))
+    for t in range(T):
+        lo, hi = o.shard_range(V, T, t)
+        got = o.embed_shard_grad(ids, g, lo, hi)
+        want = np.array(brute.embed_grad(ids.tolist(), g.tolist(), lo, hi))
+        assert got.shape == (hi - lo, H)
+        assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def pin_embed_grad_adjoint(o):
+    """The gradient is the adjoint of the (separately pinned) lookup:
+    <lookup(ids, W_r), G> == <W_r, grad(ids, G)> on every shard, in fp64."""
+    rng = np.random.default_rng(12)
+    V, T, H, n = 64, 4, 7, 300
+    W = rng.standard_normal((V, H))
+    ids = rng.integers(-5, V + 5, n)
+    G = rng.standard_normal((n, H))
+    for t in range(T):
+        lo, hi = o.shard_range(V, T, t)
+        lhs = float((o.embed_shard(ids, W[lo:hi], lo, hi) * G).sum())
+        rhs = float((W[lo:hi] * o.embed_shard_grad(ids, G, lo, hi)).sum())
+        assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs)), (t, lhs, rhs)
+
+
+def pin_embed_grad_worked_example(o):
+    """The V=8, T=2, ids [1, 6] lookup of the pages, run backwards: token 0's gradient
+    lands on shard 0's local row 1 and token 1's on shard 1's local row 6 - 4 = 2; the
+    shards' gradients side by side are the dense table's gradient (rows 1 and 6)."""
+    gfx = _golden("embed_v8_t2_ids_1_6.json")
+    V, T, ids = gfx["V"], gfx["T"], gfx["ids"]
+    G = np.array([[1.5, -2.0, 0.25], [3.0, 0.5, -1.0]])
+    dense = np.zeros((V, 3))
+    for t in range(T):
+        lo, hi = o.shard_range(V, T, t)
+        got = o.embed_shard_grad(ids, G, lo, hi)
+        want = np.zeros((hi - lo, 3))
+        for i, src in enumerate(gfx["per_shard_rows"][str(t)]):
+            if src is not None:
+                want[src - lo] += G[i]
+        assert np.array_equal(got, want), t
+        dense[lo:hi] = got
+    assert np.array_equal(dense[1], G[0]) and np.array_equal(dense[6], G[1])
+    assert not np.delete(dense, [1, 6], axis=0).any()
+
+
+def pin_embed_grad_duplicates(o):
+    """Repeated ids accumulate; ids outside [0, V) add nothing anywhere."""
+    ids = [2, 5, 2, -1, 2, 9, 5, 8, 0]
+    G = np.arange(len(ids) * 2, dtype=np.float64).reshape(-1, 2) + 1.0
+    lo, hi = 0, 5
+    got = o.embed_shard_grad(ids, G, lo, hi)
+    want = np.zeros((5, 2))
+    want[2] = G[0] + G[2] + G[4]
+    want[0] = G[8]
+    assert np.array_equal(got, want)
+    got1 = o.embed_shard_grad(ids, G, 5, 10)
+    want1 = np.zeros((5, 2))
+    want1[0] = G[1] + G[6]
+    want1[4] = G[5]
+    want1[3] = G[7]
+    assert np.array_equal(got1, want1)
+    rows = [2, 4, 0]
+    assert np.array_equal(o.embed_shard_grad_rows(ids, G, 5, rows), got1[rows])
+    assert np.array_equal(o.embed_shard_grad_rows(ids, G, 0, rows), got[rows])
 
 
 def pin_uniform_logits(o):

@@ -47,6 +47,14 @@ MUTATIONS = [
     ("        S += np.exp(z - m[:, None]).sum(axis=1)", "        S += np.exp(z - z.max(axis=1)[:, None]).sum(axis=1)"),
     # sliced dlogits: missing onehot
     ("    p[rows, t[rows] - start] -= 1.0", "    pass"),
+    # lookup gradient: repeated ids overwrite instead of accumulating
+    ("np.add.at(out, ids[own] - start, g[own])", "out[ids[own] - start] = g[own]"),
+    # lookup gradient: ids not shifted to local rows
+    ("np.add.at(out, ids[own] - start, g[own])", "np.add.at(out, np.minimum(ids[own], end - start - 1), g[own])"),
+    # lookup gradient: the shard's first id dropped
+    ("own = (ids >= start) & (ids < end)\n    np.add.at", "own = (ids > start) & (ids < end)\n    np.add.at"),
+    # lookup gradient rows: id compared without the shard start
+    ("sel = np.nonzero(ids == start + int(r))[0]", "sel = np.nonzero(ids == int(r))[0]"),
 ]
 
 
