@@ -3,7 +3,8 @@
  *
  * One vocabulary shard of a language model's tied embedding / LM-head weight,
  * W_r = rows [vocab_start, vocab_end) of the [V, H] table, is used for
- *   - the masked embedding lookup (vp_embed_fwd),
+ *   - the masked embedding lookup (vp_embed_fwd) and its weight gradient
+ *     (vp_embed_bwd),
  *   - the LM-head GEMM fused with the cross-entropy statistics, which never
  *     writes the [n, V/T] logits to memory (vp_lmhead_ce_fwd),
  *   - the merge of the T shards' statistics into the loss (vp_ce_combine),
@@ -80,6 +81,31 @@ int vp_shard_range(int64_t V, int32_t T, int32_t t, int64_t *start, int64_t *end
 int vp_embed_fwd(const int64_t *ids, int64_t n,
                  const uint16_t *w_shard, int64_t vocab_start, int64_t vocab_end, int64_t h,
                  uint16_t *out, hipStream_t stream);
+
+/* Bytes of device workspace vp_embed_bwd needs (0 when n == 0 or the sizes are invalid). Host-only. */
+size_t vp_embed_bwd_workspace(int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end);
+
+/*
+ * vp_embed_bwd -- weight gradient of one shard's masked lookup: the adjoint of
+ * vp_embed_fwd.  "5 Vocab Parallelism", 5.2.1 defines the lookup, which is linear
+ * in the shard's rows; its gradient scatters the output gradient back:
+ *   dw[ids[i] - vocab_start, :] += dout[i, :]   for every i with vocab_start <= ids[i] < vocab_end
+ * Repeated ids accumulate; tokens whose id lies outside the shard (any int64,
+ * negative included) add nothing; rows that no owned id names are left unchanged.
+ * The result is ADDED to dw, so the tied shard's LM-head gradient (vp_lmhead_ce_bwd's
+ * dw) can be passed in.  Deterministic: each row's tokens are summed in fp32 in a
+ * fixed order (increasing token index within fixed blocks of the id-sorted tokens),
+ * then added to dw once; no floating-point atomics.
+ *   ids   int64 [n]
+ *   dout  bf16  [n, h]   (gradient of vp_embed_fwd's output)
+ *   dw    fp32  [vocab_end - vocab_start, h], read and written
+ *   workspace >= vp_embed_bwd_workspace(...) bytes, 256-byte aligned, contents scratch
+ * n == 0: no-op.  Errors: NULL, SHAPE (n < 0, n > 2^24, h <= 0, more than 2^31 - 1
+ * rows), RANGE, ALIGN, WORKSPACE, HIP.
+ */
+int vp_embed_bwd(const int64_t *ids, int64_t n, const uint16_t *dout,
+                 int64_t vocab_start, int64_t vocab_end, int64_t h, float *dw,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of device workspace vp_lmhead_ce_fwd needs (0 when n == 0). Host-only. */
 size_t vp_lmhead_ce_fwd_workspace(int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end);

@@ -32,7 +32,7 @@ def _declared():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail(f"{LIB} not built (python -m vocab_lm_head_amd.build)")
+        pytest.fail(f"{LIB} not built (python vocab_lm_head_amd/build.py)")
     from vocab_lm_head_amd import _lib
     return _lib.lib
 
@@ -113,6 +113,28 @@ def test_fwd_validation_and_workspace(lib):
     assert f(*args(n=-5)) == SHAPE
     assert f(*args(hi=0)) == RANGE
     assert f(*args(n=0, x=None, w=None, t=None, ws=None, wsb=0)) == OK
+
+
+def test_embed_bwd_validation_and_workspace(lib):
+    ws = lib.vp_embed_bwd_workspace
+    n, h, vs = 65536, 4096, 64000
+    r256 = lambda b: -(-b // 256) * 256
+    nblk, nseg = -(-n // 4096), -(-n // 64)     # radix-sort tiles, segment-sum blocks
+    need = ws(n, h, 0, vs)
+    assert need == 4 * r256(4 * n) + r256(256 * nblk * 4) + 2 * r256(nseg * h * 4)
+    assert ws(0, h, 0, vs) == 0 and ws(n, 12, 0, vs) == 0 and ws(n, h, 5, 5) == 0
+    f = lib.vp_embed_bwd
+    base = dict(ids=FAKE, n=n, dout=FAKE, lo=0, hi=vs, h=h, dw=FAKE, ws=FAKE, wsb=need)
+    call = lambda **k: f(*[{**base, **k}[a] for a in ("ids", "n", "dout", "lo", "hi", "h", "dw",
+                                                      "ws", "wsb")], None)
+    assert call(ids=None) == NULL and call(dout=None) == NULL and call(dw=None) == NULL
+    assert call(n=-1) == SHAPE and call(n=(1 << 24) + 1) == SHAPE and call(h=0) == SHAPE
+    assert call(hi=0) == RANGE and call(lo=-1) == RANGE
+    assert call(h=12) == ALIGN and call(ids=FAKE + 4) == ALIGN and call(dout=FAKE + 8) == ALIGN
+    assert call(dw=FAKE + 4) == ALIGN
+    assert call(ws=None) == WORKSPACE and call(wsb=need - 1) == WORKSPACE
+    assert call(ws=FAKE + 128) == WORKSPACE
+    assert call(n=0, ids=None, dout=None, dw=None, ws=None, wsb=0) == OK
 
 
 def test_combine_validation(lib):

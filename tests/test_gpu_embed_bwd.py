@@ -1,0 +1,192 @@
+"""Weight gradient of the masked lookup (vp_embed_bwd) against the oracle's
+scatter-add, through the C ABI binding.
+
+Tolerance, derived from the arithmetic: each element of the result is dw0 plus an
+fp32 sum of the bf16 gradient values of the L tokens that own the row (exact in
+fp32 once widened), so in any summation order
+
+    |gpu - exact| <= (L + 1) * 2^-24 * (sum |x| + |dw0|)
+
+(the standard bound for recursive summation, with one more rounding for the
+addition to dw0).  That is far tighter than the 1e-2 relative bar of the LM-head
+gradients and fails on a single dropped or doubled token; the 1e-2 bar is
+checked too.  Rows that no owned id names must come back bit-for-bit unchanged.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import vp_inputs
+from gpu_util import dev_bf16, dev_i64, host, log, rel_max
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def vp():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vocab_lm_head_amd
+    return vocab_lm_head_amd
+
+
+def _run(vp, ids, dout_bits, lo, hi, dw0):
+    import torch
+    dw = torch.from_numpy(np.ascontiguousarray(dw0, dtype=np.float32)).cuda()
+    vp.vp_embed_bwd(dev_i64(ids), dev_bf16(dout_bits), lo, hi, dw)
+    torch.cuda.synchronize()
+    return dw
+
+
+def _compare(got, base, want_sum, mag_sum, count, label):
+    """got = base + the row sums, within the summation bound; rows with count 0 unchanged."""
+    want = base.astype(np.float64) + want_sum
+    bound = (count[:, None] + 1.0) * U * (np.abs(base).astype(np.float64) + mag_sum)
+    err = np.abs(got - want)
+    worst = float((err - bound).max())
+    log(f"  {label}: {len(count)} rows, max abs err {err.max():.3e}, rel {rel_max(got, want):.3e}, "
+        f"longest row {int(count.max()) if count.size else 0} tokens")
+    assert worst <= 0.0, f"{label}: error above the summation bound by {worst:.3e}"
+    assert rel_max(got, want) <= 1e-2
+    untouched = count == 0
+    assert np.array_equal(got[untouched], base[untouched].astype(np.float64)), \
+        f"{label}: a row no owned id names was modified"
+
+
+def _assert_rows(got, dw0, ids, dout, lo, rows, label):
+    """Rows `rows` (local) of the result against dw0 + the oracle's row sums."""
+    ids = np.asarray(ids, dtype=np.int64)
+    count = np.array([(ids == lo + int(r)).sum() for r in rows], dtype=np.float64)
+    _compare(got, dw0[rows], oracle.embed_shard_grad_rows(ids, dout, lo, rows),
+             oracle.embed_shard_grad_rows(ids, np.abs(dout), lo, rows), count, label)
+
+
+def _full_check(vp, ids, dout_bits, lo, hi, dw0=None, label=""):
+    """Every row of the shard against dw0 + the oracle's scatter-add."""
+    n, h = dout_bits.shape
+    ids = np.asarray(ids, dtype=np.int64)
+    dw0 = np.zeros((hi - lo, h), np.float32) if dw0 is None else dw0
+    got = host(_run(vp, ids, dout_bits, lo, hi, dw0))
+    dout = vp_inputs.bf16_bits_to_f64(dout_bits)
+    own = (ids >= lo) & (ids < hi)
+    count = np.bincount(ids[own] - lo, minlength=hi - lo).astype(np.float64)
+    _compare(got, dw0, oracle.embed_shard_grad(ids, dout, lo, hi),
+             oracle.embed_shard_grad(ids, np.abs(dout), lo, hi), count, label)
+    return got
+
+
+def _dout(seed, n, h, scale=1.0):
+    r = np.random.default_rng(seed)
+    return vp_inputs.f32_to_bf16_bits(r.standard_normal((n, h)).astype(np.float32) * scale)
+
+
+def test_worked_example_backwards(vp):
+    """V=8, T=2, ids [1, 6]: token 0's gradient is shard 0's row 1, token 1's is shard 1's
+    row 2, bit for bit; every other row stays zero."""
+    inp = vp_inputs.make_inputs("tiny")
+    wl = inp.wl
+    dout = _dout(0, 2, wl.embed_H)
+    for t in range(wl.embed_T):
+        lo, hi = vp.vp_shard_range(wl.embed_V, wl.embed_T, t)
+        got = host(_run(vp, inp.ids, dout, lo, hi, np.zeros((hi - lo, wl.embed_H), np.float32)))
+        want = oracle.embed_shard_grad(inp.ids, vp_inputs.bf16_bits_to_f64(dout), lo, hi)
+        assert np.array_equal(got, want), t
+
+
+def test_small_lm_tied_ids(vp):
+    """4096 uniform ids over V=6400 (T=2, H=512), both shards, every row."""
+    inp = vp_inputs.make_inputs("small_lm", with_weight=False)
+    wl = inp.wl
+    dout = vp_inputs.make_embed_output_grad("small_lm")
+    for t in range(wl.embed_T):
+        lo, hi = vp.vp_shard_range(wl.embed_V, wl.embed_T, t)
+        _full_check(vp, inp.ids, dout, lo, hi, label=f"small_lm shard {t}")
+
+
+def test_accumulates_and_is_deterministic(vp):
+    """The gradient is added to dw (here a random prefill), and two calls on the same
+    inputs give the same bits."""
+    r = np.random.default_rng(5)
+    n, h, lo, hi = 3000, 264, 1000, 1700
+    ids = np.minimum(r.zipf(1.2, n) + 990, 2000).astype(np.int64)
+    dout = _dout(6, n, h)
+    dw0 = r.standard_normal((hi - lo, h)).astype(np.float32)
+    a = _full_check(vp, ids, dout, lo, hi, dw0, "prefilled, Zipf ids")
+    b = host(_run(vp, ids, dout, lo, hi, dw0))
+    assert np.array_equal(a, b), "two calls differ"
+
+
+EDGE_CASES = ["all_off_shard", "one_long_row", "shard_edges", "single_token",
+              "three_passes_ragged_cols", "wide_row_two_col_blocks"]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES)
+def test_edges(vp, case):
+    r = np.random.default_rng(40 + EDGE_CASES.index(case))
+    if case == "all_off_shard":
+        n, h, lo, hi = 700, 64, 100, 200
+        ids = np.concatenate([r.integers(-50, 100, n // 2), r.integers(200, 400, n - n // 2)])
+    elif case == "one_long_row":        # one row, 5000 tokens: crosses many blocks and two sort tiles
+        n, h, lo, hi = 5000, 128, 0, 64
+        ids = np.full(n, 37, dtype=np.int64)
+    elif case == "shard_edges":
+        n, h, lo, hi = 900, 40, 512, 1024
+        edge = np.array([512, 1023, 1024, 511, -1, -100, 4096, 2**40, -2**40], dtype=np.int64)
+        ids = edge[r.integers(0, edge.size, n)]
+    elif case == "single_token":
+        n, h, lo, hi = 1, 16, 0, 10
+        ids = np.array([9], dtype=np.int64)
+    elif case == "three_passes_ragged_cols":   # Vs = 70000 needs 17-bit keys: three 8-bit passes
+        n, h, lo, hi = 9000, 8, 0, 70000
+        ids = np.concatenate([r.integers(-10, 70010, n - 2000), np.full(2000, 69999)])
+        r.shuffle(ids)
+    else:                                      # h = 2056: a full and a ragged column block
+        n, h, lo, hi = 1200, 2056, 300, 420
+        ids = r.integers(280, 440, n)
+    ids = np.asarray(ids, dtype=np.int64)
+    dout = _dout(7, n, h)
+    dw0 = r.standard_normal((hi - lo, h)).astype(np.float32)
+    log(f"  case {case}: n={n} h={h} rows={hi - lo}")
+    _full_check(vp, ids, dout, lo, hi, dw0, case)
+
+
+def test_embedding_heavy_backward(vp):
+    """65536 Zipf(1.0) ids on shard 0 ([64000, 4096] of V=256000, T=4): the 8 most
+    repeated rows, 24 other owned rows, 8 rows no id names and both shard ends, plus
+    every column's total over the shard against the owned tokens' total."""
+    import torch
+    inp = vp_inputs.make_inputs("embedding_heavy", with_weight=False)
+    wl = inp.wl
+    lo, hi = vp.vp_shard_range(wl.embed_V, wl.embed_T, 0)
+    ids = inp.ids
+    dout = vp_inputs.make_embed_output_grad("embedding_heavy")
+    dw = torch.zeros((hi - lo, wl.embed_H), dtype=torch.float32, device="cuda")
+    vp.vp_embed_bwd(dev_i64(ids), dev_bf16(dout), lo, hi, dw)
+    torch.cuda.synchronize()
+    own = (ids >= lo) & (ids < hi)
+    local = ids[own] - lo
+    rows, counts = np.unique(local, return_counts=True)
+    r = np.random.default_rng(8)
+    top = rows[np.argsort(-counts, kind="stable")[:8]]
+    others = r.choice(np.setdiff1d(rows, top), 24, replace=False)
+    untouched = r.choice(np.setdiff1d(np.arange(hi - lo), rows), 8, replace=False)
+    pick = np.unique(np.concatenate([top, others, untouched, [0, hi - lo - 1]]))
+    got = host(dw[torch.from_numpy(pick).cuda()])
+    log(f"  {own.sum()} owned ids, {rows.size} distinct rows, most repeated row x{counts.max()}")
+    # a row depends only on its own tokens: hand the oracle just those
+    sub = own & np.isin(ids - lo, pick)
+    dw0 = np.zeros((hi - lo, wl.embed_H), np.float32)
+    _assert_rows(got, dw0, ids[sub], vp_inputs.bf16_bits_to_f64(dout[sub]), lo, pick,
+                 "embedding-heavy sampled rows")
+    dout_f = vp_inputs.bf16_bits_to_f64(dout[own])
+    col_gpu = dw.double().sum(dim=0).cpu().numpy()
+    col_ref = dout_f.sum(axis=0)
+    mag = np.abs(dout_f).sum(axis=0)
+    err = np.abs(col_gpu - col_ref)
+    log(f"  column totals: max abs err {err.max():.3e}")
+    assert np.all(err <= (own.sum() + 2) * U * mag + 1e-9)

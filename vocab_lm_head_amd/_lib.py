@@ -29,6 +29,8 @@ SIGNATURES = {
     "vp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "vp_shard_range": (ctypes.c_int, [_I64, _I32, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "vp_embed_fwd": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _P]),
+    "vp_embed_bwd_workspace": (_SZ, [_I64, _I64, _I64, _I64]),
+    "vp_embed_bwd": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "vp_lmhead_ce_fwd_workspace": (_SZ, [_I64, _I64, _I64, _I64]),
     "vp_lmhead_ce_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "vp_ce_combine": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I64, _P, _P, _P, _P]),
@@ -114,6 +116,33 @@ def vp_embed_fwd(ids, w_shard, vocab_start: int, vocab_end: int, out=None, strea
     _check(lib.vp_embed_fwd(_ptr(ids), n, _ptr(w_shard), int(vocab_start), int(vocab_end), h,
                             _ptr(out), _stream(stream)), "vp_embed_fwd")
     return out
+
+
+def vp_embed_bwd_workspace(n: int, h: int, vocab_start: int, vocab_end: int) -> int:
+    return int(lib.vp_embed_bwd_workspace(n, h, vocab_start, vocab_end))
+
+
+def vp_embed_bwd(ids, dout, vocab_start: int, vocab_end: int, dw=None, workspace=None, stream=None):
+    """Lookup weight gradient of one shard, ADDED to dw (fp32 [Vs, h]; zeros if not given):
+    dw[ids[i] - start] += dout[i] for owned ids."""
+    _need(ids, torch.int64, 1, "ids")
+    _need(dout, torch.bfloat16, 2, "dout")
+    n, h = dout.shape
+    if ids.shape[0] != n:
+        raise ValueError("ids and dout must have the same number of rows")
+    vs = vocab_end - vocab_start
+    if dw is None:
+        dw = torch.zeros((vs, h), dtype=torch.float32, device=dout.device)
+    _need(dw, torch.float32, 2, "dw")
+    if tuple(dw.shape) != (vs, h):
+        raise ValueError("dw must be [vocab_end - vocab_start, h]")
+    need = vp_embed_bwd_workspace(n, h, vocab_start, vocab_end)
+    if workspace is None:
+        workspace = alloc_workspace(need, dout.device)
+    _check(lib.vp_embed_bwd(_ptr(ids), n, _ptr(dout), int(vocab_start), int(vocab_end), h,
+                            _ptr(dw), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream(stream)), "vp_embed_bwd")
+    return dw
 
 
 def vp_lmhead_ce_fwd_workspace(n: int, h: int, vocab_start: int, vocab_end: int) -> int:

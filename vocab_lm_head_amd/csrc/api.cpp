@@ -27,6 +27,11 @@ int check_shard(int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? VP_OK : VP_ERR_HIP; }
 
+// lookup gradient: token indices and sorted positions are 32-bit, and a shard's
+// row keys (plus the off-shard key) must fit 31 bits
+constexpr int64_t kEmbedBwdMaxN = (int64_t)1 << 24;
+constexpr int64_t kEmbedBwdMaxRows = ((int64_t)1 << 31) - 1;
+
 }  // namespace
 
 extern "C" {
@@ -63,6 +68,29 @@ int vp_embed_fwd(const int64_t *ids, int64_t n, const uint16_t *w_shard, int64_t
     if (!ids || !w_shard || !out) return VP_ERR_NULL;
     if (!aligned(ids, 8) || !aligned(w_shard, 16) || !aligned(out, 16)) return VP_ERR_ALIGN;
     return hip_status(vp::launch_embed(ids, n, w_shard, vocab_start, vocab_end, h, out, stream));
+}
+
+size_t vp_embed_bwd_workspace(int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end) {
+    if (n <= 0 || n > kEmbedBwdMaxN || h <= 0 || h % 8 != 0 || vocab_start < 0 ||
+        vocab_end <= vocab_start || vocab_end - vocab_start > kEmbedBwdMaxRows)
+        return 0;
+    return vp::embed_bwd_workspace(n, h).bytes;
+}
+
+int vp_embed_bwd(const int64_t *ids, int64_t n, const uint16_t *dout, int64_t vocab_start,
+                 int64_t vocab_end, int64_t h, float *dw, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+    if (n < 0 || h <= 0 || n > kEmbedBwdMaxN) return VP_ERR_SHAPE;
+    if (vocab_start < 0 || vocab_end <= vocab_start) return VP_ERR_RANGE;
+    if (vocab_end - vocab_start > kEmbedBwdMaxRows) return VP_ERR_SHAPE;
+    if (h % 8 != 0) return VP_ERR_ALIGN;
+    if (n == 0) return VP_OK;
+    if (!ids || !dout || !dw) return VP_ERR_NULL;
+    if (!aligned(ids, 8) || !aligned(dout, 16) || !aligned(dw, 16)) return VP_ERR_ALIGN;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < vp::embed_bwd_workspace(n, h).bytes)
+        return VP_ERR_WORKSPACE;
+    return hip_status(vp::launch_embed_bwd(ids, n, dout, vocab_start, vocab_end - vocab_start, h, dw,
+                                           workspace, stream));
 }
 
 size_t vp_lmhead_ce_fwd_workspace(int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end) {

@@ -28,6 +28,20 @@ BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs);
 hipError_t launch_embed(const int64_t *ids, int64_t n, const uint16_t *w, int64_t start,
                         int64_t end, int64_t h, uint16_t *out, hipStream_t stream);
 
+// lookup-gradient workspace: two (key, token) uint32 buffers for the radix sort's
+// passes, the per-tile digit counts, and fp32 [h] partials of the rows that cross
+// the segment-sum blocks (first and last row piece of each block)
+struct EmbedBwdWorkspace {
+    int64_t nblk;          // radix-sort tiles
+    int64_t nseg;          // segment-sum blocks
+    size_t off_keys[2], off_vals[2], off_hist, off_first, off_last;
+    size_t bytes;
+};
+EmbedBwdWorkspace embed_bwd_workspace(int64_t n, int64_t h);
+
+hipError_t launch_embed_bwd(const int64_t *ids, int64_t n, const uint16_t *dout, int64_t start,
+                            int64_t vs, int64_t h, float *dw, void *ws, hipStream_t stream);
+
 hipError_t launch_ce_fwd(const uint16_t *x, const uint16_t *w, const int64_t *targets, int64_t n,
                          int64_t h, int64_t start, int64_t vs, float *m_out, float *s_out,
                          float *zy_out, void *ws, hipStream_t stream);

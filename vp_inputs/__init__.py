@@ -153,6 +153,7 @@ WORKLOADS: Dict[str, Workload] = {
 # child-stream indices of the SeedSequence of a workload
 _S_X, _S_TGT, _S_IDS, _S_PERM, _S_TRIPLES, _S_EMBW = 0, 1, 2, 3, 4, 5
 _S_W0 = 8   # spawn-key prefix of the weight row blocks
+_S_DOUT0 = 9   # spawn-key prefix of the lookup's output-gradient row blocks
 _N_CHILD = 8
 
 
@@ -212,6 +213,29 @@ def make_weight_rows(wl: Workload, start: int, end: int) -> np.ndarray:
     else:
         with concurrent.futures.ThreadPoolExecutor(workers) as ex:
             list(ex.map(one_block, range(b0, b1)))
+    return out
+
+
+def make_embed_output_grad(name: str, scale: float = 1.0) -> np.ndarray:
+    """Gradient of the lookup's output, [embed_N, embed_H] bf16 bits ~ N(0, scale^2),
+    drawn in independent 1024-row blocks (like the weight) so it can be made in parallel."""
+    wl = WORKLOADS[name]
+    n, h = wl.embed_N, wl.embed_H
+    out = np.empty((n, h), dtype=np.uint16)
+
+    def one_block(b: int) -> None:
+        lo, hi = b * _ROW_BLOCK, min((b + 1) * _ROW_BLOCK, n)
+        ss = np.random.SeedSequence(entropy=wl.seed, spawn_key=(_S_DOUT0, b))
+        out[lo:hi] = _normal_bf16(np.random.Generator(np.random.PCG64(ss)), (hi - lo, h), scale)
+
+    nb = (n + _ROW_BLOCK - 1) // _ROW_BLOCK
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), nb))
+    if workers == 1:
+        for b in range(nb):
+            one_block(b)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one_block, range(nb)))
     return out
 
 
