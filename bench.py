@@ -1,6 +1,6 @@
 """Throughput of the vocab-parallel LM head + cross entropy on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-embed-bench]
 
 One step = one pass of the whole hot path over one batch of the 8B-class
 shard workload (N = 8192 tokens, H = 4096, V = 128256, T = 8, shard 0 =
@@ -14,6 +14,11 @@ shard workload (N = 8192 tokens, H = 4096, V = 128256, T = 8, shard 0 =
 The other seven shards' statistics are the other GPUs' work in a real
 deployment; they are computed once before timing.  Inputs are resident in HBM
 before the timed region.  Prints one JSON line (rank 0, N = 1).
+
+Also measured beside the step (unless --no-embed-bench): the embedding-heavy
+lookup (65536 Zipf ids on a [64000, 4096] shard) and its weight gradient, each
+against HBM bandwidth; and yardsticks (vendor GEMM, copy, fill) unless
+--no-yardsticks.
 """
 from __future__ import annotations
 
@@ -300,8 +305,11 @@ def main():
     }
 
     extra = {}
+    embed_inputs = {}
     if not args.no_embed_bench:
         extra["embedding_heavy_lookup"] = embed_bench(torch, vp, vp_inputs, dev, stream, args)
+        extra["embedding_heavy_backward"] = embed_bwd_bench(torch, vp, vp_inputs, dev, stream, args,
+                                                            keep=embed_inputs)
     if not args.no_yardsticks:
         extra["yardsticks"] = yardsticks(torch, dev, stream, N, H, Vs)
 
@@ -335,6 +343,9 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample)
+        if "embedding_heavy_backward" in result:
+            result["embedding_heavy_backward"]["cpu_baseline"] = cpu_baseline_embed_bwd(
+                embed_inputs["ids"], embed_inputs["dout"])
     print(json.dumps(result))
 
 
@@ -418,6 +429,80 @@ def embed_bench(torch, vp, vp_inputs, dev, stream, args):
             "frac": gbs / PEAK_HBM_GBS, "median_ms": ms, "min_ms": float(np.min(times)),
             "algorithmic_bytes": alg_bytes, "distinct_on_shard_rows": distinct,
             "on_shard_ids": int(own.size), "bit_exact_sample": ok}
+
+
+def embed_bwd_bench(torch, vp, vp_inputs, dev, stream, args, keep=None):
+    """Weight gradient of the embedding-heavy lookup (65536 Zipf(1.0) ids, shard 0 =
+    [64000, 4096] of V = 256000, T = 4), added into an fp32 gradient.  Algorithmic HBM
+    bytes = ids + the owned tokens' bf16 gradient rows (read once) + every distinct owned
+    row of the fp32 gradient (read and written once)."""
+    wl = vp_inputs.WORKLOADS["embedding_heavy"]
+    ids = vp_inputs.make_inputs("embedding_heavy", with_weight=False).ids
+    Vs_e = wl.embed_V // wl.embed_T
+    h = wl.embed_H
+    dout = vp_inputs.make_embed_output_grad("embedding_heavy")
+    if keep is not None:   # the CPU baseline reuses the same inputs
+        keep.update(ids=ids, dout=dout)
+    ids_d = torch.from_numpy(ids).to(dev)
+    dout_d = dev_bf16(torch, dout, dev)
+    dw = torch.zeros((Vs_e, h), dtype=torch.float32, device=dev)
+    ws = vp.alloc_workspace(vp.vp_embed_bwd_workspace(ids.shape[0], h, 0, Vs_e), dev)
+    own = (ids >= 0) & (ids < Vs_e)
+    rows, counts = np.unique(ids[own], return_counts=True)
+    alg_bytes = ids.shape[0] * 8 + int(own.sum()) * h * 2 + rows.size * h * 4 * 2
+    # check of this launch: sampled rows against plain sums of their tokens' gradients,
+    # and a second call on the same inputs giving the same bits
+    vp.vp_embed_bwd(ids_d, dout_d, 0, Vs_e, dw=dw, workspace=ws)
+    first = dw.clone()
+    dw.zero_()
+    vp.vp_embed_bwd(ids_d, dout_d, 0, Vs_e, dw=dw, workspace=ws)
+    torch.cuda.synchronize()
+    deterministic = bool(torch.equal(first, dw))
+    pick = np.concatenate([rows[np.argsort(-counts)[:4]],
+                           np.random.default_rng(9).choice(rows, 12, replace=False)])
+    got = first[torch.from_numpy(pick).to(dev)].double().cpu().numpy()
+    ref = np.stack([vp_inputs.bf16_bits_to_f64(dout[ids == r]).sum(axis=0) for r in pick])
+    sample_err = float(np.abs(got - ref).max() / np.abs(ref).max())
+    del first
+    flush = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+    times = []
+    for i in range(args.warmup + args.steps):
+        flush.sum()          # evict L2 / MALL with a read-only pass
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        vp.vp_embed_bwd(ids_d, dout_d, 0, Vs_e, dw=dw, workspace=ws)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "median_ms": ms, "min_ms": float(np.min(times)),
+            "algorithmic_bytes": alg_bytes, "owned_ids": int(own.sum()),
+            "distinct_rows": int(rows.size), "most_repeated_row": int(counts.max()),
+            "sample_max_rel_err": sample_err, "deterministic": deterministic}
+
+
+def cpu_baseline_embed_bwd(ids, dout_bits, sample_ids: int = 65536):
+    """The oracle's lookup gradient (np.add.at in fp64) on the first `sample_ids` ids of
+    the embedding-heavy lookup, shard 0; reported in the same GB/s unit as the GPU."""
+    import oracle
+    import vp_inputs
+    wl = vp_inputs.WORKLOADS["embedding_heavy"]
+    ids = ids[:sample_ids]
+    Vs_e = wl.embed_V // wl.embed_T
+    dout = vp_inputs.bf16_bits_to_f64(dout_bits[:sample_ids])
+    own = (ids >= 0) & (ids < Vs_e)
+    alg_bytes = ids.size * 8 + int(own.sum()) * wl.embed_H * 2 + \
+        np.unique(ids[own]).size * wl.embed_H * 4 * 2
+    t0 = time.perf_counter()
+    oracle.embed_shard_grad(ids, dout, 0, Vs_e)
+    dt = time.perf_counter() - t0
+    return {"value": alg_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {sample_ids} of the 65536 ids (shard 0 of [256000, 4096]): "
+                      f"np.add.at into an fp64 [64000, 4096] gradient, {dt:.2f} s"}
 
 
 if __name__ == "__main__":

@@ -14,7 +14,7 @@
 //      bit_width(Vs) bits.  A pass is three kernels: per-tile digit counts, one
 //      exclusive scan of the counts in digit-major order, and a stable scatter
 //      whose ranks come from wave ballots (tokens keep their order within a key);
-//   2. segment_sum_kernel: blocks of kSegRows sorted positions x 2048 columns.  A
+//   2. segment_sum_kernel: one wave per block of kSegRows sorted positions x 512 columns.  A
 //      row whose tokens all lie in one block is summed in token order and added
 //      to dw; the pieces of rows that cross a block edge go to per-block partials;
 //   3. segment_fixup_kernel: the block where such a row starts adds its pieces in
@@ -29,16 +29,17 @@ namespace {
 
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
-constexpr int kSortThreads = 1024;                     // 16 waves
+constexpr int kSortThreads = 256;                      // 4 waves
 constexpr int kSortRounds = 4;                         // elements per thread
+constexpr int kScanThreads = 1024;
 constexpr int kSortTile = kSortThreads * kSortRounds;  // elements per workgroup
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kSortSegs = kSortRounds * kSortWaves;    // (round, wave) groups, in element order
 
-constexpr int kSegRows = 64;        // sorted positions per segment-sum block
-constexpr int kSegThreads = 256;
+constexpr int kSegRows = 32;        // sorted positions per segment-sum block
+constexpr int kSegThreads = 64;     // one wave
 constexpr int kSegCols = 8 * kSegThreads;   // columns per block (8 bf16 = 16 bytes per thread)
-constexpr int kSegBatch = 8;        // dout rows in flight per thread
+constexpr int kSegBatch = 8;        // dout rows (and the dw rows they finish) in flight per thread
 
 // Sort key of element e: in the first pass it is made from the id, later passes
 // read the previous pass's output.
@@ -76,28 +77,50 @@ __global__ __launch_bounds__(kSortThreads) void radix_count_kernel(KeySource src
 }
 
 // In-place exclusive scan of `count` values by one workgroup: thread t scans its
-// contiguous chunk, the chunk sums are scanned in LDS, then the chunks are rewritten.
-__global__ __launch_bounds__(kSortThreads) void radix_scan_kernel(uint32_t *hist, int64_t count) {
-    __shared__ uint32_t part[2][kSortThreads];
+// contiguous chunk (read and rewritten 16 bytes at a time, kScanBatch loads in
+// flight), the chunk sums are scanned in LDS.  count is a multiple of 4 (kRadix x
+// tiles) and hist is 16-byte aligned.
+constexpr int kScanBatch = 8;
+__global__ __launch_bounds__(kScanThreads) void radix_scan_kernel(uint32_t *hist, int64_t count) {
+    __shared__ uint32_t part[2][kScanThreads];
     const int t = threadIdx.x;
-    const int64_t chunk = ceil_div(count, kSortThreads);
-    const int64_t a = t * chunk, b = min(a + chunk, count);
+    const int64_t chunk = round_up(ceil_div(count, kScanThreads), 4);
+    const int64_t a = min(t * chunk, count), b = min(a + chunk, count);
+    u32x4 *h4 = (u32x4 *)hist;
     uint32_t sum = 0;
-    for (int64_t i = a; i < b; ++i) sum += hist[i];
+    for (int64_t i = a; i < b; i += 4 * kScanBatch) {
+        u32x4 v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u)
+            v[u] = i + 4 * u < b ? h4[(i >> 2) + u] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) sum += v[u][0] + v[u][1] + v[u][2] + v[u][3];
+    }
     part[0][t] = sum;
     __syncthreads();
     int cur = 0;
-    for (int off = 1; off < kSortThreads; off <<= 1) {   // inclusive Hillis-Steele scan
+    for (int off = 1; off < kScanThreads; off <<= 1) {   // inclusive Hillis-Steele scan
         const uint32_t v = part[cur][t] + (t >= off ? part[cur][t - off] : 0u);
         part[cur ^ 1][t] = v;
         cur ^= 1;
         __syncthreads();
     }
     uint32_t run = part[cur][t] - sum;   // exclusive prefix of this chunk
-    for (int64_t i = a; i < b; ++i) {
-        const uint32_t v = hist[i];
-        hist[i] = run;
-        run += v;
+    for (int64_t i = a; i < b; i += 4 * kScanBatch) {
+        u32x4 v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u)
+            v[u] = i + 4 * u < b ? h4[(i >> 2) + u] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+            u32x4 o;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                o[c] = run;
+                run += v[u][c];
+            }
+            if (i + 4 * u < b) h4[(i >> 2) + u] = o;
+        }
     }
 }
 
@@ -178,7 +201,10 @@ __device__ __forceinline__ void store_row(float *dst, const float (&acc)[8]) {
 
 // Block (b, cb): sorted positions [b kSegRows, ...) and columns [cb kSegCols, ...).
 // Control flow depends only on the keys, which every thread reads from LDS, so it is
-// uniform; a thread past h only skips its loads and stores.
+// uniform; a thread past h only skips its loads and stores.  Whether position q ends a
+// row, and how, follows from the keys alone (sorted: the row began before the block
+// exactly when its key equals the key just before the block), so each batch issues the
+// loads of its dout rows and of the dw rows it finishes together.
 __global__ __launch_bounds__(kSegThreads) void segment_sum_kernel(
     const uint32_t *__restrict__ keys, const uint32_t *__restrict__ vals, int64_t n, uint32_t vs,
     const uint16_t *__restrict__ dout, int64_t h, float *__restrict__ dw,
@@ -199,13 +225,20 @@ __global__ __launch_bounds__(kSegThreads) void segment_sum_kernel(
     const int64_t col = (int64_t)blockIdx.y * kSegCols + 8 * t;
     const bool active = col < h;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int seg_start = 0;
     for (int q0 = 0; q0 < rows; q0 += kSegBatch) {
         u32x4 v[kSegBatch];
+        f32x4 d[kSegBatch][2];
 #pragma unroll
-        for (int u = 0; u < kSegBatch; ++u) {   // rows of this batch, loads in flight together
+        for (int u = 0; u < kSegBatch; ++u) {
             const int q = min(q0 + u, rows - 1);
+            const uint32_t key = sk[q + 1], next = sk[q + 2];
+            const bool ends = q + 1 == rows || next != key;
+            const bool direct = ends && key != vs && key != sk[0] && !(q + 1 == rows && next == key);
             v[u] = active ? *(const u32x4 *)(dout + (int64_t)sv[q] * h + col) : u32x4{0u, 0u, 0u, 0u};
+            if (active && direct && q0 + u < rows) {
+                d[u][0] = *(const f32x4 *)(dw + (int64_t)key * h + col);
+                d[u][1] = *(const f32x4 *)(dw + (int64_t)key * h + col + 4);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kSegBatch; ++u) {
@@ -216,50 +249,74 @@ __global__ __launch_bounds__(kSegThreads) void segment_sum_kernel(
             add_bf16x8(acc, v[u]);
             const uint32_t next = sk[q + 2];
             if (next == key && q + 1 < rows) continue;   // the row goes on inside the block
-            const bool before = seg_start == 0 && sk[0] == key;
+            const bool before = sk[0] == key;
             const bool after = next == key;              // only possible at the block's end
             if (active) {
-                if (!before && !after) add_to_row(dw + (int64_t)key * h + col, acc);
-                else if (before) store_row(part_first + b * h + col, acc);
-                else store_row(part_last + b * h + col, acc);
+                if (!before && !after) {
+                    d[u][0] += f32x4{acc[0], acc[1], acc[2], acc[3]};
+                    d[u][1] += f32x4{acc[4], acc[5], acc[6], acc[7]};
+                    *(f32x4 *)(dw + (int64_t)key * h + col) = d[u][0];
+                    *(f32x4 *)(dw + (int64_t)key * h + col + 4) = d[u][1];
+                } else if (before) {
+                    store_row(part_first + b * h + col, acc);
+                } else {
+                    store_row(part_last + b * h + col, acc);
+                }
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[c] = 0.f;
-            seg_start = q + 1;
         }
     }
 }
 
 // Rows that cross block edges: the block where such a row starts (its last row goes
 // on into the next block, and did not come from the previous one) adds the row's
-// pieces in block order, then adds the total to dw.
-__global__ __launch_bounds__(kSegThreads) void segment_fixup_kernel(
+// pieces in block order, then adds the total to dw.  One workgroup per block; most
+// blocks have no such row and return after reading three keys.  The blocks the row
+// reaches into are contiguous (the keys are sorted), so the workgroup counts them with
+// one boundary test per thread, then sums their pieces with independent loads.
+constexpr int kFixThreads = 256;
+constexpr int kFixBatch = 8;
+__global__ __launch_bounds__(kFixThreads) void segment_fixup_kernel(
     const uint32_t *__restrict__ keys, int64_t n, uint32_t vs, int64_t h, float *__restrict__ dw,
     const float *__restrict__ part_first, const float *__restrict__ part_last) {
     const int64_t b = blockIdx.x;
     const int64_t p0 = b * kSegRows, p1 = min(p0 + kSegRows, n);
     if (p1 >= n) return;
-    const uint32_t key = keys[p1 - 1];
-    if (key == vs || keys[p1] != key) return;           // no row goes on past this block
-    if (p0 > 0 && keys[p0 - 1] == key) return;          // it started in an earlier block
-    const int64_t col = (int64_t)blockIdx.y * kSegCols + 8 * threadIdx.x;
-    if (col >= h) return;
-    float acc[8];
-    {
-        const f32x4 a = *(const f32x4 *)(part_last + b * h + col);
-        const f32x4 c = *(const f32x4 *)(part_last + b * h + col + 4);
-        acc[0] = a[0]; acc[1] = a[1]; acc[2] = a[2]; acc[3] = a[3];
-        acc[4] = c[0]; acc[5] = c[1]; acc[6] = c[2]; acc[7] = c[3];
+    // the three boundary keys are loaded together: one memory latency for the many
+    // blocks that return here
+    const uint32_t key = keys[p1 - 1], next = keys[p1], prev = p0 > 0 ? keys[p0 - 1] : vs;
+    if (key == vs || next != key) return;               // no row goes on past this block
+    if (prev == key) return;                            // it started in an earlier block
+    // m = number of following blocks that start with this row's key
+    int64_t m = 0;
+    for (;;) {
+        const int64_t q = (b + 1 + m + threadIdx.x) * kSegRows;
+        const int c = __syncthreads_count(q < n && keys[q] == key);
+        m += c;
+        if (c < kFixThreads) break;
     }
-    for (int64_t b2 = b + 1;; ++b2) {
-        const f32x4 a = *(const f32x4 *)(part_first + b2 * h + col);
-        const f32x4 c = *(const f32x4 *)(part_first + b2 * h + col + 4);
-        acc[0] += a[0]; acc[1] += a[1]; acc[2] += a[2]; acc[3] += a[3];
-        acc[4] += c[0]; acc[5] += c[1]; acc[6] += c[2]; acc[7] += c[3];
-        const int64_t q1 = min((b2 + 1) * kSegRows, n);
-        if (q1 >= n || keys[q1] != key) break;           // the row ends in block b2
+    for (int64_t col = 8 * threadIdx.x; col < h; col += 8 * kFixThreads) {
+        f32x4 lo = *(const f32x4 *)(part_last + b * h + col);
+        f32x4 hi = *(const f32x4 *)(part_last + b * h + col + 4);
+        for (int64_t j0 = 1; j0 <= m; j0 += kFixBatch) {
+            f32x4 a[kFixBatch], c[kFixBatch];
+#pragma unroll
+            for (int u = 0; u < kFixBatch; ++u) {
+                const int64_t j = min(j0 + u, m);
+                a[u] = *(const f32x4 *)(part_first + (b + j) * h + col);
+                c[u] = *(const f32x4 *)(part_first + (b + j) * h + col + 4);
+            }
+#pragma unroll
+            for (int u = 0; u < kFixBatch; ++u)
+                if (j0 + u <= m) {
+                    lo += a[u];
+                    hi += c[u];
+                }
+        }
+        const float acc[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        add_to_row(dw + (int64_t)key * h + col, acc);
     }
-    add_to_row(dw + (int64_t)key * h + col, acc);
 }
 
 int radix_passes(int64_t vs) {   // digits needed for keys 0 .. vs (vs = off-shard)
@@ -306,7 +363,7 @@ hipError_t launch_embed_bwd(const int64_t *ids, int64_t n, const uint16_t *dout,
                       start, (uint32_t)vs};
         hipLaunchKernelGGL(radix_count_kernel, dim3(nblk), dim3(kSortThreads), 0, stream, src, n,
                            p * kRadixBits, hist, nblk);
-        hipLaunchKernelGGL(radix_scan_kernel, dim3(1), dim3(kSortThreads), 0, stream, hist,
+        hipLaunchKernelGGL(radix_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, hist,
                            (int64_t)kRadix * nblk);
         hipLaunchKernelGGL(radix_scatter_kernel, dim3(nblk), dim3(kSortThreads), 0, stream, src, n,
                            p * kRadixBits, hist, nblk, keys[p & 1], vals[p & 1]);
@@ -316,8 +373,8 @@ hipError_t launch_embed_bwd(const int64_t *ids, int64_t n, const uint16_t *dout,
     const dim3 grid((unsigned)w.nseg, (unsigned)ceil_div(h, kSegCols));
     hipLaunchKernelGGL(segment_sum_kernel, grid, dim3(kSegThreads), 0, stream, sk, sv, n,
                        (uint32_t)vs, dout, h, dw, first, last);
-    hipLaunchKernelGGL(segment_fixup_kernel, grid, dim3(kSegThreads), 0, stream, sk, n, (uint32_t)vs,
-                       h, dw, first, last);
+    hipLaunchKernelGGL(segment_fixup_kernel, dim3((unsigned)w.nseg), dim3(kFixThreads), 0, stream, sk,
+                       n, (uint32_t)vs, h, dw, first, last);
     return hipGetLastError();
 }
 
