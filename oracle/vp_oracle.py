@@ -34,7 +34,7 @@ import numpy as np
 DEFAULT_IGNORE_INDEX = -100
 
 __all__ = [
-    "DEFAULT_IGNORE_INDEX", "shard_range", "embed_shard", "embed_shard_grad",
+    "DEFAULT_IGNORE_INDEX", "shard_range", "padded_vocab", "embed_shard", "embed_shard_grad",
     "embed_shard_grad_rows", "logits",
     "shard_stats", "combine_triples", "pages_sharded_ce", "dense_ce",
     "dense_dlogits", "shard_grads", "mean_scale", "lse_dense_chunked",
@@ -57,6 +57,18 @@ def shard_range(V: int, T: int, t: int):
         raise ValueError(f"V={V} is not divisible by T={T}")
     vs = V // T
     return t * vs, (t + 1) * vs
+
+
+def padded_vocab(V: int, T: int, multiple: int = 128) -> int:
+    """Vocabulary size after padding so that every shard's V/T rows are a multiple of
+    ``multiple``: the smallest V_pad >= V divisible by multiple * T (interview note
+    "Vocab parallelism", the padding question: GPT-2's 50257 becomes 51200 for 8 ranks).
+    The extra rows are ordinary rows of the table that no id or target uses; the method
+    then runs unchanged on V_pad (5.1 holds since T divides V_pad)."""
+    if V <= 0 or T < 1 or multiple < 1:
+        raise ValueError(f"bad padding request V={V} T={T} multiple={multiple}")
+    q = multiple * T
+    return -(-V // q) * q
 
 
 def embed_shard(ids, w_shard: np.ndarray, start: int, end: int) -> np.ndarray:

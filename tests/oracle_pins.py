@@ -55,6 +55,28 @@ def pin_shard_range(o):
         raise AssertionError(f"shard_range{bad} must fail")
 
 
+def pin_padded_vocab(o):
+    """The pages' example (50257 -> 51200 for 8 ranks, each shard 6400 = 50 x 128 rows),
+    plus the defining properties: divisible, shard rows a multiple of 128, minimal."""
+    g = _golden("vocab_padding.json")
+    assert o.padded_vocab(g["V"], g["T"], g["multiple"]) == g["V_pad"]
+    rng = np.random.default_rng(21)
+    for V, T, m in [(8, 2, 1), (16032 * 8, 8, 128), (1, 1, 128), (1000, 3, 128)] + \
+            [(int(rng.integers(1, 10**6)), int(rng.integers(1, 17)), int(rng.choice([1, 64, 128, 256])))
+             for _ in range(200)]:
+        vp = o.padded_vocab(V, T, m)
+        assert vp >= V and vp % T == 0 and (vp // T) % m == 0, (V, T, m, vp)
+        assert vp - V < m * T, (V, T, m, vp)
+        if V % (m * T) == 0:
+            assert vp == V
+    for bad in [(0, 8, 128), (100, 0, 128), (100, 8, 0)]:
+        try:
+            o.padded_vocab(*bad)
+        except ValueError:
+            continue
+        raise AssertionError(f"padded_vocab{bad} must fail")
+
+
 def _check_lookup_golden(o, g):
     V, T, ids = g["V"], g["T"], g["ids"]
     H = 5

@@ -47,6 +47,10 @@ MUTATIONS = [
     ("        S += np.exp(z - m[:, None]).sum(axis=1)", "        S += np.exp(z - z.max(axis=1)[:, None]).sum(axis=1)"),
     # sliced dlogits: missing onehot
     ("    p[rows, t[rows] - start] -= 1.0", "    pass"),
+    # padding: round up to a multiple of the per-shard quantum only (not x T)
+    ("    q = multiple * T\n", "    q = multiple\n"),
+    # padding: round to nearest instead of up
+    ("    return -(-V // q) * q", "    return max(q, round(V / q) * q)"),
     # lookup gradient: repeated ids overwrite instead of accumulating
     ("np.add.at(out, ids[own] - start, g[own])", "out[ids[own] - start] = g[own]"),
     # lookup gradient: ids not shifted to local rows
