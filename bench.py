@@ -15,7 +15,8 @@ The other seven shards' statistics are the other GPUs' work in a real
 deployment; they are computed once before timing.  Inputs are resident in HBM
 before the timed region.  Prints one JSON line (rank 0, N = 1).
 
-Also measured beside the step (unless --no-embed-bench): the embedding-heavy
+Also measured beside the step (unless --no-embed-bench): the step's CE sequence on
+the padded vocabulary (shard 0 = 16128 rows instead of 16032), the embedding-heavy
 lookup (65536 Zipf ids on a [64000, 4096] shard) and its weight gradient, each
 against HBM bandwidth; and yardsticks (vendor GEMM, copy, fill) unless
 --no-yardsticks.
@@ -305,6 +306,9 @@ def main():
     }
 
     extra = {}
+    if not args.no_embed_bench:
+        extra["vocab_padding"] = padding_bench(torch, vp, dev, stream, args, x_d, w_full, y_d, m, s,
+                                               zy, loss, lse, mean, dx, grad_scale, ce_ms)
     embed_inputs = {}
     if not args.no_embed_bench:
         extra["embedding_heavy_lookup"] = embed_bench(torch, vp, vp_inputs, dev, stream, args)
@@ -429,6 +433,42 @@ def embed_bench(torch, vp, vp_inputs, dev, stream, args):
             "frac": gbs / PEAK_HBM_GBS, "median_ms": ms, "min_ms": float(np.min(times)),
             "algorithmic_bytes": alg_bytes, "distinct_on_shard_rows": distinct,
             "on_shard_ids": int(own.size), "bit_exact_sample": ok}
+
+
+def padding_bench(torch, vp, dev, stream, args, x_d, w_full, y_d, m, s, zy, loss, lse, mean, dx,
+                  grad_scale, unpadded_ms):
+    """The pages' padding tip at the 8B-class shard: V = 128256 padded for T = 8 to
+    vp_padded_vocab(128256, 8, 128) = 129024, i.e. shard 0 = 16128 = 126 x 128 rows instead
+    of 16032.  Times the same fwd + combine + bwd sequence at the padded size (rows of the
+    same weight) beside the unpadded one: both shards are 63 vocabulary tiles of 256."""
+    N, H = x_d.shape
+    V_pad = vp.vp_padded_vocab(128256, 8, 128)
+    vs = V_pad // 8
+    w0 = w_full[:vs]
+    dw = torch.empty((vs, H), dtype=torch.float32, device=dev)
+    ws_f = vp.alloc_workspace(vp.vp_lmhead_ce_fwd_workspace(N, H, 0, vs), dev)
+    ws_b = vp.alloc_workspace(vp.vp_lmhead_ce_bwd_workspace(N, H, 0, vs), dev)
+
+    def step():
+        vp.vp_lmhead_ce_fwd(x_d, w0, y_d, 0, vs, m[0], s[0], zy[0], workspace=ws_f)
+        vp.vp_ce_combine(m, s, zy, y_d, loss=loss, lse=lse, loss_mean=mean)
+        vp.vp_lmhead_ce_bwd(x_d, w0, y_d, lse, 0, vs, grad_scale, dx=dx, dw=dw, workspace=ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    return {"V": 128256, "V_pad": V_pad, "shard_rows": 16032, "padded_shard_rows": vs,
+            "unpadded_ms": unpadded_ms, "padded_ms": ms,
+            "padded_over_unpadded": ms / unpadded_ms,
+            "note": "same 63 vocabulary tiles either way: the kernels mask the shard's tail "
+                    "rows in-tile, so padding buys no speed here"}
 
 
 def embed_bwd_bench(torch, vp, vp_inputs, dev, stream, args, keep=None):

@@ -67,6 +67,18 @@ const char *vp_status_string(int status);
 int vp_shard_range(int64_t V, int32_t T, int32_t t, int64_t *start, int64_t *end);
 
 /*
+ * vp_padded_vocab -- vocabulary size after padding so that every shard's rows are a
+ * multiple of `multiple` (the interview note "Vocab parallelism", padding question:
+ * each rank's V/t a multiple of 128; GPT-2's 50257 becomes 51200 for 8 ranks):
+ *   V_pad = the smallest multiple of multiple * T that is >= V.
+ * The extra rows are ordinary rows of the (padded) table that no id or target uses;
+ * every other entry point then runs unchanged with V_pad in place of V.
+ *   V, T, multiple : host scalars, all >= 1.   V_pad : host pointer receiving the size.
+ * Errors: VP_ERR_NULL, VP_ERR_SHAPE (V <= 0, T < 1, multiple < 1, or overflow).
+ */
+int vp_padded_vocab(int64_t V, int32_t T, int64_t multiple, int64_t *V_pad);
+
+/*
  * vp_embed_fwd -- masked vocab-parallel embedding lookup of one shard.
  * "5 Vocab Parallelism", 5.2.1; interview note, Figure 1:
  *   out[i, :] = w_shard[ids[i] - vocab_start, :]  if vocab_start <= ids[i] < vocab_end

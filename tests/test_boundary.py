@@ -73,6 +73,26 @@ def test_shard_range(lib):
     assert lib.vp_shard_range(8, 2, 0, None, ctypes.byref(b)) == NULL
 
 
+def test_padded_vocab_matches_the_oracle(lib):
+    """Host-only helper: the pages' 50257 -> 51200 (T = 8) and random sizes, against the
+    oracle's definition; bad arguments are rejected."""
+    import numpy as np
+
+    import oracle
+    out = ctypes.c_int64()
+    assert lib.vp_padded_vocab(50257, 8, 128, ctypes.byref(out)) == OK and out.value == 51200
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        V, T, m = int(rng.integers(1, 10**9)), int(rng.integers(1, 65)), int(rng.choice([1, 8, 128, 256]))
+        assert lib.vp_padded_vocab(V, T, m, ctypes.byref(out)) == OK
+        assert out.value == oracle.padded_vocab(V, T, m), (V, T, m)
+    assert lib.vp_padded_vocab(0, 8, 128, ctypes.byref(out)) == SHAPE
+    assert lib.vp_padded_vocab(100, 0, 128, ctypes.byref(out)) == SHAPE
+    assert lib.vp_padded_vocab(100, 8, 0, ctypes.byref(out)) == SHAPE
+    assert lib.vp_padded_vocab(2**62, 8, 2**60, ctypes.byref(out)) == SHAPE
+    assert lib.vp_padded_vocab(100, 8, 128, None) == NULL
+
+
 FAKE = 0x10000          # 256-byte aligned, never dereferenced (validation fails first)
 FAKE_ODD = 0x10002
 

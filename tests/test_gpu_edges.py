@@ -136,6 +136,26 @@ def test_twelve_shards_full_path(vp):
     _full_check(vp, xb, wb, y, T=12, bwd_shards=[0, 5, 11], label="T=12")
 
 
+@pytest.mark.parametrize("pad_rows", ["random", "zero"])
+def test_padded_vocabulary(vp, pad_rows):
+    """The pages' padding example: GPT-2's V = 50257 padded to 51200 for T = 8 (each shard
+    6400 = 50 x 128 rows).  The extra rows are ordinary rows no target uses (random or zero
+    weights); the whole path runs on V_pad and matches the oracle's dense CE over V_pad."""
+    V, T = 50257, 8
+    V_pad = vp.vp_padded_vocab(V, T, 128)
+    assert V_pad == 51200
+    r = np.random.default_rng(50257)
+    N, H = 300, 64
+    xb = vp_inputs.f32_to_bf16_bits(r.standard_normal((N, H)).astype(np.float32))
+    w = r.standard_normal((V_pad, H)).astype(np.float32) * (3.0 / math.sqrt(H))
+    if pad_rows == "zero":
+        w[V:] = 0.0
+    wb = vp_inputs.f32_to_bf16_bits(w)
+    y = r.integers(0, V, N).astype(np.int64)
+    y[:8] = V - 1                        # the last real id, in the shard holding the padding
+    _full_check(vp, xb, wb, y, T=T, bwd_shards=[0, 7], label=f"V_pad=51200 ({pad_rows} padding)")
+
+
 def test_large_logits(vp):
     """Logit std 40: the stabilising maximum matters; sum-exp must not overflow."""
     xb, wb, y = _problem(7, 130, 128, 640, logit_std=40.0)

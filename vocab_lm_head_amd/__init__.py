@@ -8,5 +8,6 @@ fallback.
 from ._lib import (  # noqa: F401
     DEFAULT_IGNORE_INDEX, VPError, alloc_workspace, lib, status_string, vp_ce_combine,
     vp_embed_bwd, vp_embed_bwd_workspace, vp_embed_fwd, vp_lmhead_ce_bwd,
-    vp_lmhead_ce_bwd_workspace, vp_lmhead_ce_fwd, vp_lmhead_ce_fwd_workspace, vp_shard_range,
+    vp_lmhead_ce_bwd_workspace, vp_lmhead_ce_fwd, vp_lmhead_ce_fwd_workspace, vp_padded_vocab,
+    vp_shard_range,
 )

@@ -28,6 +28,7 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "vp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "vp_shard_range": (ctypes.c_int, [_I64, _I32, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "vp_padded_vocab": (ctypes.c_int, [_I64, _I32, _I64, ctypes.POINTER(_I64)]),
     "vp_embed_fwd": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _P]),
     "vp_embed_bwd_workspace": (_SZ, [_I64, _I64, _I64, _I64]),
     "vp_embed_bwd": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
@@ -99,6 +100,13 @@ def vp_shard_range(V: int, T: int, t: int):
     _check(lib.vp_shard_range(int(V), int(T), int(t), ctypes.byref(a), ctypes.byref(b)),
            "vp_shard_range")
     return a.value, b.value
+
+
+def vp_padded_vocab(V: int, T: int, multiple: int = 128) -> int:
+    """Smallest V_pad >= V with every one of the T shards a multiple of `multiple` rows."""
+    out = _I64()
+    _check(lib.vp_padded_vocab(int(V), int(T), int(multiple), ctypes.byref(out)), "vp_padded_vocab")
+    return out.value
 
 
 def vp_embed_fwd(ids, w_shard, vocab_start: int, vocab_end: int, out=None, stream=None):

@@ -59,6 +59,15 @@ int vp_shard_range(int64_t V, int32_t T, int32_t t, int64_t *start, int64_t *end
     return VP_OK;
 }
 
+int vp_padded_vocab(int64_t V, int32_t T, int64_t multiple, int64_t *V_pad) {
+    if (!V_pad) return VP_ERR_NULL;
+    if (V <= 0 || T < 1 || multiple < 1 || multiple > INT64_MAX / T) return VP_ERR_SHAPE;
+    const int64_t q = multiple * T;
+    if (V > INT64_MAX - (q - 1)) return VP_ERR_SHAPE;
+    *V_pad = (V + q - 1) / q * q;
+    return VP_OK;
+}
+
 int vp_embed_fwd(const int64_t *ids, int64_t n, const uint16_t *w_shard, int64_t vocab_start,
                  int64_t vocab_end, int64_t h, uint16_t *out, hipStream_t stream) {
     if (n < 0 || h <= 0) return VP_ERR_SHAPE;
