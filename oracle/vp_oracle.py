@@ -36,7 +36,7 @@ DEFAULT_IGNORE_INDEX = -100
 __all__ = [
     "DEFAULT_IGNORE_INDEX", "shard_range", "padded_vocab", "embed_shard", "embed_shard_grad",
     "embed_shard_grad_rows", "logits",
-    "shard_stats", "combine_triples", "pages_sharded_ce", "dense_ce",
+    "shard_stats", "shard_sumexp", "combine_triples", "pages_sharded_ce", "dense_ce",
     "dense_dlogits", "shard_grads", "mean_scale", "lse_dense_chunked",
     "shard_stats_chunked", "dz_rows", "dz_cols",
 ]
@@ -153,6 +153,14 @@ def shard_stats(z_shard: np.ndarray, targets, start: int):
     rows = np.nonzero(own)[0]
     zy[rows] = z[rows, t[rows] - start]
     return m, s, zy
+
+
+def shard_sumexp(z_shard: np.ndarray, m_ref) -> np.ndarray:
+    """The second pass of the pages' order ("5 Vocab Parallelism", 5.3.1): one shard's
+    sum of exp(z - m) about a given per-token maximum m (the global one, after the
+    all-reduce MAX)."""
+    z = np.asarray(z_shard, dtype=np.float64)
+    return np.exp(z - np.asarray(m_ref, dtype=np.float64)[:, None]).sum(axis=1)
 
 
 def combine_triples(m, s, zy, targets, ignore_index: int = DEFAULT_IGNORE_INDEX):

@@ -260,6 +260,24 @@ def pin_sharded_equals_dense(o):
             assert abs(mean2 - ref_mean) < 1e-12
 
 
+def pin_shard_sumexp_two_pass(o):
+    """The pages' two-pass order from per-shard pieces: the global max of the shards' local
+    maxima, then each shard's sum about it; their total reproduces the dense lse, and merged
+    with the combine (every shard's max set to the global one) the dense loss."""
+    x, w, y = _rand_problem(31, 40, 12, 60, scale=4.0, ignore_frac=0.1)
+    z = o.logits(x, w)
+    loss, lse, mean = o.dense_ce(z, y)
+    T = 5
+    bounds = [o.shard_range(60, T, t) for t in range(T)]
+    M = np.max(np.stack([o.shard_stats(z[:, a:b], y, a)[0] for a, b in bounds]), axis=0)
+    assert np.allclose(M, z.max(axis=1), rtol=0, atol=0)
+    s = np.stack([o.shard_sumexp(z[:, a:b], M) for a, b in bounds])
+    assert np.allclose(M + np.log(s.sum(axis=0)), lse, rtol=0, atol=1e-12)
+    zy = np.stack([o.shard_stats(z[:, a:b], y, a)[2] for a, b in bounds])
+    l2, lse2, mean2 = o.combine_triples(np.broadcast_to(M, s.shape), s, zy, y)
+    assert np.allclose(l2, loss, rtol=0, atol=1e-12) and abs(mean2 - mean) < 1e-12
+
+
 def pin_torch_cross_entropy(o):
     import torch
     import torch.nn.functional as F

@@ -47,6 +47,9 @@ MUTATIONS = [
     ("        S += np.exp(z - m[:, None]).sum(axis=1)", "        S += np.exp(z - z.max(axis=1)[:, None]).sum(axis=1)"),
     # sliced dlogits: missing onehot
     ("    p[rows, t[rows] - start] -= 1.0", "    pass"),
+    # two-pass order: sum about the shard's own maximum instead of the given one
+    ("    return np.exp(z - np.asarray(m_ref, dtype=np.float64)[:, None]).sum(axis=1)",
+     "    return np.exp(z - z.max(axis=1)[:, None]).sum(axis=1)"),
     # padding: round up to a multiple of the per-shard quantum only (not x T)
     ("    q = multiple * T\n", "    q = multiple\n"),
     # padding: round to nearest instead of up
