@@ -15,7 +15,9 @@ The other seven shards' statistics are the other GPUs' work in a real
 deployment; they are computed once before timing.  Inputs are resident in HBM
 before the timed region.  Prints one JSON line (rank 0, N = 1).
 
-Also measured beside the step (unless --no-embed-bench): the step's CE sequence on
+Also measured beside the step: the same CE sequence with the shard's logits stored
+in HBM instead of fused (the pages' tensor-parallel baseline; --no-comparator skips
+it); and, unless --no-embed-bench, the step's CE sequence on
 the padded vocabulary (shard 0 = 16128 rows instead of 16032), the embedding-heavy
 lookup (65536 Zipf ids on a [64000, 4096] shard) and its weight gradient, each
 against HBM bandwidth; and yardsticks (vendor GEMM, copy, fill) unless
@@ -81,6 +83,16 @@ CE_KERNELS = ("CeStatsEpilogue", "merge_slices_kernel", "combine_kernel", "mean_
               "transpose_bf16_kernel", "DlogitsEpilogue", "StoreTransposedEpilogue")
 
 
+def short_kernel_name(name: str) -> str:
+    """A kernel's short name in profiler output: the epilogue of a GEMM instance
+    (gemm_nt_kernel<...Epilogue>), otherwise the function's own name."""
+    m = re.search(r"gemm_nt_kernel<(?:[\w:]*::)?(?:\(anonymous namespace\)::)?(\w+)>", name)
+    if m:
+        return m.group(1)
+    m = re.search(r"(\w+)\(", name)
+    return m.group(1) if m else name
+
+
 def _pmc_rows(path, counter):
     """[(dispatch id, short kernel name, value)] of one counter, summed over its dimensions."""
     acc = {}
@@ -88,10 +100,7 @@ def _pmc_rows(path, counter):
         if r["Counter_Name"] != counter:
             continue
         k = int(r["Dispatch_Id"])
-        n = r["Kernel_Name"]
-        m = re.search(r"namespace\)::(\w+)", n)
-        short = m.group(1) if m else n.split("(")[0]
-        acc.setdefault(k, [short, 0.0])[1] += float(r["Counter_Value"])
+        acc.setdefault(k, [short_kernel_name(r["Kernel_Name"]), 0.0])[1] += float(r["Counter_Value"])
     return sorted((k, v[0], v[1]) for k, v in acc.items())
 
 
@@ -178,13 +187,15 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=8192)
     ap.add_argument("--no-embed-bench", action="store_true")
     ap.add_argument("--no-yardsticks", action="store_true")
+    ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--reduce-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script into profiles/ and exit (no GPU needed)")
     args = ap.parse_args()
     if args.reduce_pmc:
         base = "rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{d} -o run -- " \
-               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-embed-bench"
+               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-embed-bench " \
+               "--no-comparator"
         reduce_pmc(args.reduce_pmc[0], args.reduce_pmc[1], base.format(c="FETCH_SIZE", d="fetch"),
                    base.format(c="WRITE_SIZE", d="write"))
         return
@@ -306,6 +317,10 @@ def main():
     }
 
     extra = {}
+    if not args.no_comparator:
+        extra["materialised_logits_comparator"] = comparator_bench(
+            torch, vp, dev, stream, args, x_d, w0, y_d, m, s, zy, loss, lse, mean, dx, dw,
+            grad_scale, ce_ms, avg, ws_f, ws_b)
     if not args.no_embed_bench:
         extra["vocab_padding"] = padding_bench(torch, vp, dev, stream, args, x_d, w_full, y_d, m, s,
                                                zy, loss, lse, mean, dx, grad_scale, ce_ms)
@@ -433,6 +448,63 @@ def embed_bench(torch, vp, vp_inputs, dev, stream, args):
             "frac": gbs / PEAK_HBM_GBS, "median_ms": ms, "min_ms": float(np.min(times)),
             "algorithmic_bytes": alg_bytes, "distinct_on_shard_rows": distinct,
             "on_shard_ids": int(own.size), "bit_exact_sample": ok}
+
+
+def comparator_bench(torch, vp, dev, stream, args, x_d, w0, y_d, m, s, zy, loss, lse, mean, dx, dw,
+                     grad_scale, fused_ms, fused_avg, ws_f, ws_b):
+    """The same CE sequence with shard 0's fp32 logits stored in HBM (the pages'
+    tensor-parallel baseline) instead of fused: logits GEMM, statistics read back from them
+    (in one read, or in the pages' order: maxima, all-reduce MAX, sums about the global
+    maximum), combine, and the backward from the stored logits (no recompute).  Reports
+    time and the device memory beyond the inputs and gradients, beside the fused path."""
+    N, H = x_d.shape
+    Vs = w0.shape[0]
+    logits = torch.empty((N, vp.logits_ld(Vs)), dtype=torch.float32, device=dev)
+    M = torch.empty(N, dtype=torch.float32, device=dev)
+
+    def fwd(two_pass):
+        vp.vp_lmhead_logits(x_d, w0, 0, Vs, logits=logits)
+        vp.vp_logits_ce_stats(logits, y_d, 0, Vs, None, m[0], s[0], zy[0])
+        if two_pass:
+            vp.vp_ce_max(m, out=M)
+            vp.vp_logits_ce_stats(logits, y_d, 0, Vs, M, m[0], s[0], zy[0])
+
+    def step(two_pass, marks=None):
+        if marks:
+            marks[0].record(stream)
+        fwd(two_pass)
+        if marks:
+            marks[1].record(stream)
+        vp.vp_ce_combine(m, s, zy, y_d, loss=loss, lse=lse, loss_mean=mean)
+        if marks:
+            marks[2].record(stream)
+        vp.vp_logits_ce_bwd(logits, x_d, w0, y_d, lse, 0, Vs, grad_scale, dx=dx, dw=dw,
+                            workspace=ws_b)
+        if marks:
+            marks[3].record(stream)
+
+    out = {}
+    for two_pass in (False, True):
+        for _ in range(args.warmup):
+            step(two_pass)
+        marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            step(two_pass, marks[k])
+        torch.cuda.synchronize()
+        parts = [float(np.mean([mk[i].elapsed_time(mk[i + 1]) for mk in marks])) for i in range(3)]
+        out["two_pass" if two_pass else "one_read"] = {
+            "ms": sum(parts), "fwd_ms": parts[0], "combine_ms": parts[1], "bwd_ms": parts[2]}
+    logits_bytes = logits.numel() * 4
+    out.update({
+        "fused_ms": fused_ms, "fused_fwd_ms": fused_avg["fwd"], "fused_bwd_ms": fused_avg["bwd"],
+        "stored_logits_bytes": logits_bytes,
+        "fused_fwd_workspace_bytes": ws_f.numel(),
+        "bwd_workspace_bytes": ws_b.numel(),
+        "extra_memory_vs_fused_bytes": logits_bytes - ws_f.numel(),
+        "note": "the fused path never stores the [N, Vs] logits and recomputes them in the "
+                "backward; the comparator stores them in fp32 and skips the recompute GEMM"})
+    return out
 
 
 def padding_bench(torch, vp, dev, stream, args, x_d, w_full, y_d, m, s, zy, loss, lse, mean, dx,

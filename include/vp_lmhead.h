@@ -184,6 +184,44 @@ int vp_lmhead_ce_bwd(const uint16_t *hidden, const uint16_t *w_shard, const int6
                      float grad_scale, float *dx, float *dw,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------
+ * Materialised-logits comparator.  The same step with one shard's logits stored in HBM,
+ * as the pages' tensor-parallel baseline holds them ([S, B, V/T] per rank, fp32).  Not the
+ * fused hot path: it exists to measure the memory and time the fused path saves
+ * ("5 Vocab Parallelism", 5.3.1-5.3.2).  Conventions as above; ld_logits is the row
+ * stride of the [n, ld_logits] fp32 logits, a multiple of 4 with Vs <= ld_logits <= 2^20 + 1024.
+ * ------------------------------------------------------------------------------------ */
+
+/* logits[i, j] = (hidden w_shard^T)[i, j] for j < Vs, fp32 (columns Vs .. round_up(Vs, 4)
+ * are written with zeros).  n == 0: no-op.  Errors: NULL, SHAPE, RANGE, ALIGN, HIP. */
+int vp_lmhead_logits(const uint16_t *hidden, const uint16_t *w_shard, int64_t n, int64_t h,
+                     int64_t vocab_start, int64_t vocab_end, float *logits, int64_t ld_logits,
+                     hipStream_t stream);
+
+/* Per-token statistics of one shard's stored logits (5.3.1):
+ *   m_ref == NULL: m_local = max_j z, s_local = sum_j exp(z - m_local)  (one read);
+ *   m_ref != NULL: m_local = m_ref, s_local = sum_j exp(z - m_ref)      (the pages' second
+ *                  pass, m_ref = the global maximum from vp_ce_max);
+ *   zy_local = z[targets - vocab_start] if the target lies in the shard, else 0.
+ * The outputs feed vp_ce_combine unchanged.  n == 0: no-op.
+ * Errors: NULL, SHAPE (n or Vs above 2^20), RANGE, ALIGN, HIP. */
+int vp_logits_ce_stats(const float *logits, int64_t ld_logits, const int64_t *targets, int64_t n,
+                       int64_t vocab_start, int64_t vocab_end, const float *m_ref,
+                       float *m_local, float *s_local, float *zy_local, hipStream_t stream);
+
+/* m_max[i] = max_r m[r, i] over the T rows of m [T, n] (the all-reduce MAX of 5.3.1 on one
+ * GPU).  n == 0: no-op.  Errors: NULL, SHAPE, ALIGN, HIP. */
+int vp_ce_max(const float *m, int64_t n, int32_t T, float *m_max, hipStream_t stream);
+
+/* Backward from the stored logits (5.3.2): dz = g (exp(z - lse) - onehot) read from logits
+ * instead of recomputed, then dx and dw exactly as vp_lmhead_ce_bwd (same arguments,
+ * semantics and workspace: vp_lmhead_ce_bwd_workspace). */
+int vp_logits_ce_bwd(const float *logits, int64_t ld_logits, const uint16_t *hidden,
+                     const uint16_t *w_shard, const int64_t *targets, const float *lse, int64_t n,
+                     int64_t h, int64_t vocab_start, int64_t vocab_end, int64_t ignore_index,
+                     float grad_scale, float *dx, float *dw, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import oracle
+
 LOSS_ATOL = 2e-3
 GRAD_RTOL = 1e-2
 STAT_ATOL = 2e-3
@@ -94,3 +96,17 @@ def run_ce_path(vp, x_d, w_shards_d, starts, ends, tgt_d, grad_scale, bwd_shards
                                        grad_scale, ignore_index)
     torch.cuda.synchronize()
     return {"loss": loss, "lse": lse, "mean": mean, "m": m, "s": s, "zy": zy, "grads": grads}
+
+
+def sampled_grads(out, t, x, w_shard, y, lse_ref, start, g, rng, k_rows=24, k_cols=24):
+    """Compare sampled rows of dX_t and dW_t with the oracle evaluated on those rows."""
+    n, vs = x.shape[0], w_shard.shape[0]
+    rows = np.unique(np.concatenate([rng.choice(n, k_rows, replace=False), [0, n - 1]]))
+    dzr = oracle.dz_rows(x[rows], w_shard, y[rows], lse_ref[rows], start, g)
+    assert_grad_close(host(out["grads"][t][0][rows]), dzr @ w_shard, f"dX_{t} ({rows.size} rows)")
+    # vocabulary rows: random ones, both ends, and rows that are targets
+    own = y[(y >= start) & (y < start + vs)] - start
+    cols = np.unique(np.concatenate([rng.choice(vs, k_cols, replace=False), [0, vs - 1],
+                                     own[:8]])).astype(np.int64)
+    dzc = oracle.dz_cols(x, w_shard[cols], cols + start, y, lse_ref, g)
+    assert_grad_close(host(out["grads"][t][1][cols]), dzc.T @ x, f"dW_{t} ({cols.size} rows)")

@@ -157,6 +157,33 @@ def test_embed_bwd_validation_and_workspace(lib):
     assert call(n=0, ids=None, dout=None, dw=None, ws=None, wsb=0) == OK
 
 
+def test_comparator_validation(lib):
+    n, h, vs = 8192, 4096, 16032
+    f = lib.vp_lmhead_logits
+    assert f(FAKE, FAKE, n, h, 0, vs, FAKE, vs - 4, None) == SHAPE      # ld < Vs
+    assert f(FAKE, FAKE, n, h, 0, vs, FAKE, vs + 2, None) == ALIGN      # ld % 4
+    assert f(FAKE, FAKE, n, h, 0, vs, FAKE, (1 << 21), None) == SHAPE   # ld too large
+    assert f(None, FAKE, n, h, 0, vs, FAKE, vs, None) == NULL
+    assert f(FAKE, FAKE, n, h, 0, vs, FAKE + 4, vs, None) == ALIGN
+    assert f(None, None, 0, h, 0, vs, None, vs, None) == OK
+    g = lib.vp_logits_ce_stats
+    assert g(FAKE, vs, FAKE, n, 0, vs, None, FAKE, FAKE, None, None) == NULL
+    assert g(FAKE, vs, FAKE, n, 10, 10, None, FAKE, FAKE, FAKE, None) == RANGE
+    assert g(FAKE, vs - 4, FAKE, n, 0, vs, None, FAKE, FAKE, FAKE, None) == SHAPE
+    assert g(FAKE, vs, FAKE + 4, n, 0, vs, None, FAKE, FAKE, FAKE, None) == ALIGN
+    assert g(FAKE, vs, FAKE, n, 0, vs, FAKE + 2, FAKE, FAKE, FAKE, None) == ALIGN
+    m = lib.vp_ce_max
+    assert m(FAKE, n, 0, FAKE, None) == SHAPE and m(None, n, 8, FAKE, None) == NULL
+    assert m(None, 0, 8, None, None) == OK
+    b = lib.vp_logits_ce_bwd
+    ws = lib.vp_lmhead_ce_bwd_workspace(n, h, 0, vs)
+    args = [FAKE, vs, FAKE, FAKE, FAKE, FAKE, n, h, 0, vs, -100, 1.0, FAKE, FAKE, FAKE, ws, None]
+    call = lambda i, v: b(*(args[:i] + [v] + args[i + 1:]))
+    assert call(0, None) == NULL and call(1, vs - 4) == SHAPE and call(1, vs + 1) == ALIGN
+    assert call(15, ws - 1) == WORKSPACE and call(14, None) == WORKSPACE
+    assert call(13, FAKE + 4) == ALIGN
+
+
 def test_combine_validation(lib):
     f = lib.vp_ce_combine
     assert f(FAKE, FAKE, FAKE, FAKE, 16, 0, -100, FAKE, FAKE, FAKE, None) == SHAPE

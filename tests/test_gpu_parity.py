@@ -18,7 +18,7 @@ import pytest
 import oracle
 import vp_inputs
 from gpu_util import (assert_grad_close, assert_loss_close, assert_stats_close, bf16_bits,
-                      dev_bf16, dev_i64, host, log, run_ce_path)
+                      dev_bf16, dev_i64, host, log, run_ce_path, sampled_grads)
 
 pytestmark = pytest.mark.gpu
 
@@ -122,20 +122,6 @@ def test_small_lm(vp):
         assert_grad_close(host(out["grads"][t][1]), dwr, f"dW shard {t}")
 
 
-def _sampled_grads(out, t, x, w_shard, y, lse_ref, start, g, rng, k_rows=24, k_cols=24):
-    """Compare sampled rows of dX_t and dW_t with the oracle evaluated on those rows."""
-    n, vs = x.shape[0], w_shard.shape[0]
-    rows = np.unique(np.concatenate([rng.choice(n, k_rows, replace=False), [0, n - 1]]))
-    dzr = oracle.dz_rows(x[rows], w_shard, y[rows], lse_ref[rows], start, g)
-    assert_grad_close(host(out["grads"][t][0][rows]), dzr @ w_shard, f"dX_{t} ({rows.size} rows)")
-    # vocabulary rows: random ones, both ends, and rows that are targets
-    own = y[(y >= start) & (y < start + vs)] - start
-    cols = np.unique(np.concatenate([rng.choice(vs, k_cols, replace=False), [0, vs - 1],
-                                     own[:8]])).astype(np.int64)
-    dzc = oracle.dz_cols(x, w_shard[cols], cols + start, y, lse_ref, g)
-    assert_grad_close(host(out["grads"][t][1][cols]), dzc.T @ x, f"dW_{t} ({cols.size} rows)")
-
-
 def _golden(name):
     path = os.path.join(GOLDEN, f"oracle_{name}.npz")
     if not os.path.exists(path):
@@ -167,7 +153,7 @@ def test_shard_8b(vp):
         ref = oracle.shard_stats(oracle.logits(x[sample], wt), y[sample], a)
         assert_stats_close((host(out["m"][t][sample]), host(out["s"][t][sample]),
                             host(out["zy"][t][sample])), ref, f"shard {t} stats (64 tokens)")
-        _sampled_grads(out, t, x, wt, y, gold["lse"], a, g, r)
+        sampled_grads(out, t, x, wt, y, gold["lse"], a, g, r)
     # tied lookup of shard 0 with Zipf ids
     _embed_case(vp, inp.ids, inp.w, wl.V, wl.T, [0, 5])
 
@@ -199,7 +185,7 @@ def test_large_vocab(vp):
     ref = oracle.shard_stats(oracle.logits(x[sample], w0), y[sample], 0)
     assert_stats_close((host(out["m"][0][sample]), host(out["s"][0][sample]),
                         host(out["zy"][0][sample])), ref, "shard 0 stats (48 tokens)")
-    _sampled_grads(out, 0, x, w0, y, gold["lse"], 0, g, r, k_rows=16, k_cols=16)
+    sampled_grads(out, 0, x, w0, y, gold["lse"], 0, g, r, k_rows=16, k_cols=16)
 
 
 def test_large_vocab_combine_synthetic(vp):
@@ -243,4 +229,4 @@ def test_embedding_heavy(vp):
     ref = oracle.shard_stats(oracle.logits(x[sample], w), y[sample], 0)
     assert_stats_close((host(out["m"][0][sample]), host(out["s"][0][sample]),
                         host(out["zy"][0][sample])), ref, "stats (32 tokens)")
-    _sampled_grads(out, 0, x, w, y, gold["lse"], 0, g, r, k_rows=12, k_cols=24)
+    sampled_grads(out, 0, x, w, y, gold["lse"], 0, g, r, k_rows=12, k_cols=24)

@@ -38,6 +38,11 @@ SIGNATURES = {
     "vp_lmhead_ce_bwd_workspace": (_SZ, [_I64, _I64, _I64, _I64]),
     "vp_lmhead_ce_bwd": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
                                         ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "vp_lmhead_logits": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P]),
+    "vp_logits_ce_stats": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "vp_ce_max": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
+    "vp_logits_ce_bwd": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                        ctypes.c_float, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -238,4 +243,83 @@ def vp_lmhead_ce_bwd(hidden, w_shard, targets, lse, vocab_start: int, vocab_end:
                                 float(grad_scale), _ptr(dx), _ptr(dw), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)),
            "vp_lmhead_ce_bwd")
+    return dx, dw
+
+
+# ---------------------------------------------------------------------------
+# materialised-logits comparator (not the fused path; it measures what that path saves)
+def logits_ld(vs: int) -> int:
+    """Row stride of stored fp32 logits: Vs rounded up to a multiple of 4."""
+    return -(-int(vs) // 4) * 4
+
+
+def vp_lmhead_logits(hidden, w_shard, vocab_start: int, vocab_end: int, logits=None, stream=None):
+    """fp32 logits [n, ld] of one shard (columns past Vs are zero)."""
+    _need(hidden, torch.bfloat16, 2, "hidden")
+    _need(w_shard, torch.bfloat16, 2, "w_shard")
+    n, h = hidden.shape
+    vs = vocab_end - vocab_start
+    if w_shard.shape != (vs, h):
+        raise ValueError("w_shard must be [vocab_end - vocab_start, h]")
+    if logits is None:
+        logits = torch.empty((n, logits_ld(vs)), dtype=torch.float32, device=hidden.device)
+    _need(logits, torch.float32, 2, "logits")
+    if logits.shape[0] != n:
+        raise ValueError("logits must have n rows")
+    _check(lib.vp_lmhead_logits(_ptr(hidden), _ptr(w_shard), n, h, int(vocab_start), int(vocab_end),
+                                _ptr(logits), logits.shape[1], _stream(stream)), "vp_lmhead_logits")
+    return logits
+
+
+def vp_logits_ce_stats(logits, targets, vocab_start: int, vocab_end: int, m_ref=None,
+                       m_local=None, s_local=None, zy_local=None, stream=None):
+    """(m, s, zy) fp32 [n] of one shard from its stored logits; with m_ref, s is taken
+    about m_ref (the pages' second pass)."""
+    _need(logits, torch.float32, 2, "logits")
+    _need(targets, torch.int64, 1, "targets")
+    n = logits.shape[0]
+    dev = logits.device
+    outs = []
+    for t in (m_local, s_local, zy_local):
+        t = torch.empty(n, dtype=torch.float32, device=dev) if t is None else t
+        _need(t, torch.float32, 1, "statistics output")
+        outs.append(t)
+    if m_ref is not None:
+        _need(m_ref, torch.float32, 1, "m_ref")
+    _check(lib.vp_logits_ce_stats(_ptr(logits), logits.shape[1], _ptr(targets), n, int(vocab_start),
+                                  int(vocab_end), _ptr(m_ref), _ptr(outs[0]), _ptr(outs[1]),
+                                  _ptr(outs[2]), _stream(stream)), "vp_logits_ce_stats")
+    return tuple(outs)
+
+
+def vp_ce_max(m, out=None, stream=None):
+    """Per-token maximum over the T rows of m [T, n]."""
+    _need(m, torch.float32, 2, "m")
+    T, n = m.shape
+    out = torch.empty(n, dtype=torch.float32, device=m.device) if out is None else out
+    _need(out, torch.float32, 1, "out")
+    _check(lib.vp_ce_max(_ptr(m), n, T, _ptr(out), _stream(stream)), "vp_ce_max")
+    return out
+
+
+def vp_logits_ce_bwd(logits, hidden, w_shard, targets, lse, vocab_start: int, vocab_end: int,
+                     grad_scale: float, ignore_index: int = DEFAULT_IGNORE_INDEX,
+                     dx=None, dw=None, workspace=None, stream=None):
+    """(dx partial [n, h], dw [Vs, h]) fp32 from the stored logits (no recompute)."""
+    _need(logits, torch.float32, 2, "logits")
+    _need(hidden, torch.bfloat16, 2, "hidden")
+    _need(w_shard, torch.bfloat16, 2, "w_shard")
+    n, h = hidden.shape
+    vs = vocab_end - vocab_start
+    dev = hidden.device
+    dx = torch.empty((n, h), dtype=torch.float32, device=dev) if dx is None else dx
+    dw = torch.empty((vs, h), dtype=torch.float32, device=dev) if dw is None else dw
+    need = vp_lmhead_ce_bwd_workspace(n, h, vocab_start, vocab_end)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib.vp_logits_ce_bwd(_ptr(logits), logits.shape[1], _ptr(hidden), _ptr(w_shard),
+                                _ptr(targets), _ptr(lse), n, h, int(vocab_start), int(vocab_end),
+                                int(ignore_index), float(grad_scale), _ptr(dx), _ptr(dw),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream)), "vp_logits_ce_bwd")
     return dx, dw

@@ -23,7 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvplmhead.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "embed.hip", "embed_bwd.hip", "ce_fwd.hip", "ce_combine.hip", "ce_bwd.hip"]
+SOURCES = ["api.cpp", "embed.hip", "embed_bwd.hip", "ce_fwd.hip", "ce_combine.hip", "ce_bwd.hip",
+           "logits.hip"]
 
 # packed-fp32 VALU forms are disabled on purpose: the compiler would otherwise
 # emit them from plain float code in the epilogues.

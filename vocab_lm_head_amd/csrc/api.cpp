@@ -27,6 +27,10 @@ int check_shard(int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? VP_OK : VP_ERR_HIP; }
 
+// stored logits: the fp32 store epilogue addresses 256 token rows of ld elements through
+// one 1 GiB buffer resource
+constexpr int64_t kMaxLogitsLd = ((int64_t)1 << 20) + 1024;
+
 // lookup gradient: token indices and sorted positions are 32-bit, and a shard's
 // row keys (plus the off-shard key) must fit 31 bits
 constexpr int64_t kEmbedBwdMaxN = (int64_t)1 << 24;
@@ -167,6 +171,73 @@ int vp_lmhead_ce_bwd(const uint16_t *hidden, const uint16_t *w_shard, const int6
     }
     return hip_status(vp::launch_ce_bwd(hidden, w_shard, targets, lse, n, h, vocab_start, vs,
                                         ignore_index, grad_scale, dx, dw, workspace, stream));
+}
+
+// ---- materialised-logits comparator ----------------------------------------------------
+
+int vp_lmhead_logits(const uint16_t *hidden, const uint16_t *w_shard, int64_t n, int64_t h,
+                     int64_t vocab_start, int64_t vocab_end, float *logits, int64_t ld_logits,
+                     hipStream_t stream) {
+    int st = check_shard(n, h, vocab_start, vocab_end);
+    if (st != VP_OK) return st;
+    const int64_t vs = vocab_end - vocab_start;
+    if (ld_logits < vs || ld_logits > kMaxLogitsLd) return VP_ERR_SHAPE;
+    if (ld_logits % 4 != 0) return VP_ERR_ALIGN;
+    if (n == 0) return VP_OK;
+    if (!hidden || !w_shard || !logits) return VP_ERR_NULL;
+    if (!aligned(hidden, 16) || !aligned(w_shard, 16) || !aligned(logits, 16)) return VP_ERR_ALIGN;
+    return hip_status(vp::launch_lmhead_logits(hidden, w_shard, n, h, vs, logits, ld_logits, stream));
+}
+
+int vp_logits_ce_stats(const float *logits, int64_t ld_logits, const int64_t *targets, int64_t n,
+                       int64_t vocab_start, int64_t vocab_end, const float *m_ref, float *m_local,
+                       float *s_local, float *zy_local, hipStream_t stream) {
+    if (n < 0 || n > (1 << 20)) return VP_ERR_SHAPE;
+    if (vocab_start < 0 || vocab_end <= vocab_start) return VP_ERR_RANGE;
+    const int64_t vs = vocab_end - vocab_start;
+    if (vs > (1 << 20) || ld_logits < vs || ld_logits > kMaxLogitsLd) return VP_ERR_SHAPE;
+    if (ld_logits % 4 != 0) return VP_ERR_ALIGN;
+    if (n == 0) return VP_OK;
+    if (!logits || !targets || !m_local || !s_local || !zy_local) return VP_ERR_NULL;
+    if (!aligned(logits, 16) || !aligned(targets, 8) || !aligned(m_local, 4) ||
+        !aligned(s_local, 4) || !aligned(zy_local, 4) || (m_ref && !aligned(m_ref, 4)))
+        return VP_ERR_ALIGN;
+    return hip_status(vp::launch_logits_stats(logits, ld_logits, targets, n, vocab_start, vs, m_ref,
+                                              m_local, s_local, zy_local, stream));
+}
+
+int vp_ce_max(const float *m, int64_t n, int32_t T, float *m_max, hipStream_t stream) {
+    if (n < 0 || T < 1 || n > ((int64_t)1 << 31)) return VP_ERR_SHAPE;
+    if (n == 0) return VP_OK;
+    if (!m || !m_max) return VP_ERR_NULL;
+    if (!aligned(m, 4) || !aligned(m_max, 4)) return VP_ERR_ALIGN;
+    return hip_status(vp::launch_rows_max(m, n, T, m_max, stream));
+}
+
+int vp_logits_ce_bwd(const float *logits, int64_t ld_logits, const uint16_t *hidden,
+                     const uint16_t *w_shard, const int64_t *targets, const float *lse, int64_t n,
+                     int64_t h, int64_t vocab_start, int64_t vocab_end, int64_t ignore_index,
+                     float grad_scale, float *dx, float *dw, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    int st = check_shard(n, h, vocab_start, vocab_end);
+    if (st != VP_OK) return st;
+    const int64_t vs = vocab_end - vocab_start;
+    if (ld_logits < vs || ld_logits > kMaxLogitsLd) return VP_ERR_SHAPE;
+    if (ld_logits % 4 != 0) return VP_ERR_ALIGN;
+    if (!dw) return VP_ERR_NULL;
+    if (!aligned(dw, 16)) return VP_ERR_ALIGN;
+    if (n > 0) {
+        if (!logits || !hidden || !w_shard || !targets || !lse || !dx) return VP_ERR_NULL;
+        if (!aligned(logits, 16) || !aligned(hidden, 16) || !aligned(w_shard, 16) ||
+            !aligned(targets, 8) || !aligned(lse, 4) || !aligned(dx, 16))
+            return VP_ERR_ALIGN;
+        if (!workspace || !aligned(workspace, 256) ||
+            workspace_bytes < vp::bwd_workspace(n, h, vs).bytes)
+            return VP_ERR_WORKSPACE;
+    }
+    return hip_status(vp::launch_logits_ce_bwd(logits, ld_logits, hidden, w_shard, targets, lse, n, h,
+                                               vocab_start, vs, ignore_index, grad_scale, dx, dw,
+                                               workspace, stream));
 }
 
 }  // extern "C"

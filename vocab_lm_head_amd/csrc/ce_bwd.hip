@@ -191,32 +191,6 @@ struct DlogitsEpilogue {
     }
 };
 
-// out[n, m] = C[m, n] (fp32), m < M, n < N; M a multiple of 4.  Stores go through a
-// resource over the output rows from the workgroup's first one: rows past N are
-// outside it, columns past M get an offset outside it.
-struct StoreTransposedEpilogue {
-    float *out;
-    int64_t ldo;
-    int M, N;
-
-    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane, int m0,
-                                               int n0, uint16_t *) const {
-        const int rsub = 4 * (lane >> 4);
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(out + (int64_t)n0 * ldo + m0, ((int64_t)(N - n0) * ldo - m0) * 4);
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) {
-            const int64_t nl = nbase - n0 + 16 * j + (lane & 15);
-#pragma unroll
-            for (int i = 0; i < kTM; ++i) {
-                const int ml = mbase - m0 + 16 * i + rsub;
-                store16<kStoreDefault>(__builtin_bit_cast(u32x4, acc[i][j]), rs,
-                        m0 + ml < M ? (uint32_t)((nl * ldo + ml) * 4) : kOutOfRange);
-            }
-        }
-    }
-};
-
 __global__ void fill_zero_kernel(float *p, int64_t count) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -245,34 +219,24 @@ BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs) {
     return b;
 }
 
-hipError_t launch_ce_bwd(const uint16_t *x, const uint16_t *w, const int64_t *targets,
-                         const float *lse, int64_t n, int64_t h, int64_t start, int64_t vs,
-                         int64_t ignore_index, float grad_scale, float *dx, float *dw, void *ws,
-                         hipStream_t stream) {
-    if (n == 0) {   // no tokens: the weight gradient is zero, dx has no rows
-        const int64_t cnt = vs * h;
-        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(cnt, 256), 8192)),
-                           dim3(256), 0, stream, dw, cnt);
-        return hipGetLastError();
-    }
+hipError_t launch_bwd_transposes(const uint16_t *x, const uint16_t *w, int64_t n, int64_t h,
+                                 int64_t vs, void *ws, hipStream_t stream) {
     const BwdWorkspace b = bwd_workspace(n, h, vs);
     char *base = (char *)ws;
-    uint16_t *xt = (uint16_t *)(base + b.off_xt);
-    uint16_t *wt = (uint16_t *)(base + b.off_wt);
-    uint16_t *dz = (uint16_t *)(base + b.off_dz);
-    uint16_t *dzt = (uint16_t *)(base + b.off_dzt);
     hipError_t e;
-    if ((e = transpose_bf16(x, n, h, xt, b.n_ld, stream)) != hipSuccess) return e;
-    if ((e = transpose_bf16(w, vs, h, wt, b.vs_ld, stream)) != hipSuccess) return e;
+    if ((e = transpose_bf16(x, n, h, (uint16_t *)(base + b.off_xt), b.n_ld, stream)) != hipSuccess)
+        return e;
+    return transpose_bf16(w, vs, h, (uint16_t *)(base + b.off_wt), b.vs_ld, stream);
+}
 
-    {   // recompute + dlogits: rows = vocab (A = W_r), cols = tokens (B = X)
-        const GemmGrid g = gemm_grid(vs, n);
-        DlogitsEpilogue epi{targets, lse, start, ignore_index, grad_scale, (int)vs, (int)n,
-                            b.vs_ld, b.n_ld, dz, dzt};
-        hipLaunchKernelGGL(gemm_nt_kernel<DlogitsEpilogue>, dim3(g.blocks()), dim3(kThreads), 0,
-                           stream, Operand{w, h, (int)vs}, Operand{x, h, (int)n}, (int)h,
-                           g.tiles_m, g.tiles_n, epi);
-    }
+hipError_t launch_bwd_grad_gemms(int64_t n, int64_t h, int64_t vs, float *dx, float *dw, void *ws,
+                                 hipStream_t stream) {
+    const BwdWorkspace b = bwd_workspace(n, h, vs);
+    char *base = (char *)ws;
+    const uint16_t *xt = (const uint16_t *)(base + b.off_xt);
+    const uint16_t *wt = (const uint16_t *)(base + b.off_wt);
+    const uint16_t *dz = (const uint16_t *)(base + b.off_dz);
+    const uint16_t *dzt = (const uint16_t *)(base + b.off_dzt);
     {   // dX_r^T [H, N] = W_r^T [H, Vs64] . dz [N, Vs64]^T
         const GemmGrid g = gemm_grid(h, n);
         StoreTransposedEpilogue epi{dx, h, (int)h, (int)n};
@@ -288,6 +252,36 @@ hipError_t launch_ce_bwd(const uint16_t *x, const uint16_t *w, const int64_t *ta
                            (int)b.n_ld, g.tiles_m, g.tiles_n, epi);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_bwd_zero_dw(float *dw, int64_t vs, int64_t h, hipStream_t stream) {
+    const int64_t cnt = vs * h;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(cnt, 256), 8192)),
+                       dim3(256), 0, stream, dw, cnt);
+    return hipGetLastError();
+}
+
+hipError_t launch_ce_bwd(const uint16_t *x, const uint16_t *w, const int64_t *targets,
+                         const float *lse, int64_t n, int64_t h, int64_t start, int64_t vs,
+                         int64_t ignore_index, float grad_scale, float *dx, float *dw, void *ws,
+                         hipStream_t stream) {
+    if (n == 0) return launch_bwd_zero_dw(dw, vs, h, stream);   // no tokens: dW is zero
+    const BwdWorkspace b = bwd_workspace(n, h, vs);
+    char *base = (char *)ws;
+    uint16_t *dz = (uint16_t *)(base + b.off_dz);
+    uint16_t *dzt = (uint16_t *)(base + b.off_dzt);
+    hipError_t e;
+    if ((e = launch_bwd_transposes(x, w, n, h, vs, ws, stream)) != hipSuccess) return e;
+    {   // recompute + dlogits: rows = vocab (A = W_r), cols = tokens (B = X)
+        const GemmGrid g = gemm_grid(vs, n);
+        DlogitsEpilogue epi{targets, lse, start, ignore_index, grad_scale, (int)vs, (int)n,
+                            b.vs_ld, b.n_ld, dz, dzt};
+        hipLaunchKernelGGL(gemm_nt_kernel<DlogitsEpilogue>, dim3(g.blocks()), dim3(kThreads), 0,
+                           stream, Operand{w, h, (int)vs}, Operand{x, h, (int)n}, (int)h,
+                           g.tiles_m, g.tiles_n, epi);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_bwd_grad_gemms(n, h, vs, dx, dw, ws, stream);
 }
 
 }  // namespace vp

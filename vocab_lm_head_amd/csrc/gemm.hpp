@@ -265,6 +265,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(Operand A, Operand
     gemm_nt_tile(A, B, K, tiles_m, tiles_n, epi, blockIdx.x, smem);
 }
 
+// out[n, m] = C[m, n] (fp32), m < M, n < N.  Stores are 4 rows of C (16 bytes) at a time:
+// when M is not a multiple of 4, the last chunk also writes C's zero rows past M into the
+// row's padding, so ldo must be a multiple of 4 (>= M).  Stores go through a
+// resource over the output rows from the workgroup's first one: rows past N are
+// outside it, columns past M get an offset outside it.
+struct StoreTransposedEpilogue {
+    float *out;
+    int64_t ldo;
+    int M, N;
+
+    __device__ __forceinline__ void operator()(Acc &acc, int mbase, int nbase, int lane, int m0,
+                                               int n0, uint16_t *) const {
+        const int rsub = 4 * (lane >> 4);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(out + (int64_t)n0 * ldo + m0, ((int64_t)(N - n0) * ldo - m0) * 4);
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int64_t nl = nbase - n0 + 16 * j + (lane & 15);
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const int ml = mbase - m0 + 16 * i + rsub;
+                store16<kStoreDefault>(__builtin_bit_cast(u32x4, acc[i][j]), rs,
+                        m0 + ml < M ? (uint32_t)((nl * ldo + ml) * 4) : kOutOfRange);
+            }
+        }
+    }
+};
+
 // Launch geometry of a GEMM over an M x N output.
 struct GemmGrid {
     int tiles_m, tiles_n;

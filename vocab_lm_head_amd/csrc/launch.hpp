@@ -50,6 +50,27 @@ hipError_t launch_ce_combine(const float *m, const float *s, const float *zy,
                              const int64_t *targets, int64_t n, int T, int64_t ignore_index,
                              float *loss, float *lse, float *loss_mean, hipStream_t stream);
 
+// pieces of the backward shared with the materialised-logits comparator: X^T and W^T into
+// the workspace; the dX and dW GEMMs from the workspace's dz and dz^T; dW = 0 for n == 0
+hipError_t launch_bwd_transposes(const uint16_t *x, const uint16_t *w, int64_t n, int64_t h,
+                                 int64_t vs, void *ws, hipStream_t stream);
+hipError_t launch_bwd_grad_gemms(int64_t n, int64_t h, int64_t vs, float *dx, float *dw, void *ws,
+                                 hipStream_t stream);
+hipError_t launch_bwd_zero_dw(float *dw, int64_t vs, int64_t h, hipStream_t stream);
+
+// materialised-logits comparator
+hipError_t launch_lmhead_logits(const uint16_t *x, const uint16_t *w, int64_t n, int64_t h,
+                                int64_t vs, float *logits, int64_t ld, hipStream_t stream);
+hipError_t launch_logits_stats(const float *logits, int64_t ld, const int64_t *targets, int64_t n,
+                               int64_t start, int64_t vs, const float *m_ref, float *m_out,
+                               float *s_out, float *zy_out, hipStream_t stream);
+hipError_t launch_rows_max(const float *m, int64_t n, int T, float *out, hipStream_t stream);
+hipError_t launch_logits_ce_bwd(const float *logits, int64_t ld, const uint16_t *x,
+                                const uint16_t *w, const int64_t *targets, const float *lse,
+                                int64_t n, int64_t h, int64_t start, int64_t vs,
+                                int64_t ignore_index, float grad_scale, float *dx, float *dw,
+                                void *ws, hipStream_t stream);
+
 hipError_t launch_ce_bwd(const uint16_t *x, const uint16_t *w, const int64_t *targets,
                          const float *lse, int64_t n, int64_t h, int64_t start, int64_t vs,
                          int64_t ignore_index, float grad_scale, float *dx, float *dw, void *ws,
