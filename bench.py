@@ -89,7 +89,7 @@ def short_kernel_name(name: str) -> str:
     m = re.search(r"gemm_nt_kernel<(?:[\w:]*::)?(?:\(anonymous namespace\)::)?(\w+)>", name)
     if m:
         return m.group(1)
-    m = re.search(r"(\w+)\(", name)
+    m = re.search(r"(\w+)(?:<[^<>()]*>)?\(", name)
     return m.group(1) if m else name
 
 
