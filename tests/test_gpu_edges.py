@@ -156,6 +156,32 @@ def test_padded_vocabulary(vp, pad_rows):
     _full_check(vp, xb, wb, y, T=T, bwd_shards=[0, 7], label=f"V_pad=51200 ({pad_rows} padding)")
 
 
+@pytest.mark.parametrize("shape", [(1, 64, 40, 2), (257, 64, 514, 2), (255, 8, 255, 1)])
+def test_tile_boundaries(vp, shape):
+    """A single token, and sizes one past / one short of a 256-row tile in both the token
+    and the vocabulary dimension (N, H, V, T), H down to 8."""
+    N, H, V, T = shape
+    xb, wb, y = _problem(1000 + N, N, H, V, logit_std=3.0)
+    _full_check(vp, xb, wb, y, T=T, label=f"N={N} H={H} V={V}")
+
+
+def test_deterministic(vp):
+    """The forward, combine and backward use no atomics: two calls on the same inputs give
+    the same bits (statistics, loss, lse, mean, dX, dW)."""
+    import torch
+    xb, wb, y = _problem(77, 700, 136, 1200, logit_std=4.0, ignore_frac=0.1)
+    x_d, w_d, y_d = dev_bf16(xb), dev_bf16(wb), dev_i64(y)
+    rng = [oracle.shard_range(1200, 3, t) for t in range(3)]
+    g = oracle.mean_scale(y)
+    runs = [run_ce_path(vp, x_d, [w_d[a:b] for a, b in rng], [a for a, _ in rng],
+                        [b for _, b in rng], y_d, g, bwd_shards=[0, 2]) for _ in range(2)]
+    for key in ("m", "s", "zy", "loss", "lse", "mean"):
+        assert torch.equal(runs[0][key], runs[1][key]), key
+    for t in (0, 2):
+        for k in range(2):
+            assert torch.equal(runs[0]["grads"][t][k], runs[1]["grads"][t][k]), (t, k)
+
+
 def test_large_logits(vp):
     """Logit std 40: the stabilising maximum matters; sum-exp must not overflow."""
     xb, wb, y = _problem(7, 130, 128, 640, logit_std=40.0)

@@ -23,8 +23,10 @@
 //
 // Rows past M / N read as zeros (outside the buffer resource; the epilogue
 // masks them); K chunks past K are zero-filled, so K need only be a multiple
-// of 8.  Operands must have 16-byte aligned rows, and a 256-row panel must
-// stay below 2 GiB (ld < 4M elements) so that byte offsets fit 32 bits.
+// of 8.  Operands must have 16-byte aligned rows.  Buffer resources are capped
+// at 1 GiB (kResourceCap), which holds every byte a 256-row panel's K steps
+// reach as long as rows are at most ~2M elements; the C ABI keeps n, h and Vs
+// (hence every operand row) at or below 2^20 + 64 elements.
 #pragma once
 
 #include "common.hpp"
