@@ -10,9 +10,14 @@
  *   - the merge of the T shards' statistics into the loss (vp_ce_combine),
  *     which stands in for the three per-token all-reduces of the method,
  *   - the local backward: dlogits = softmax - onehot, then dX_r and dW_r
- *     (vp_lmhead_ce_bwd).
+ *     (vp_lmhead_ce_bwd),
+ *   - the vocabulary padding of the interview note (vp_padded_vocab), and a
+ *     materialised-logits comparator that stores the shard's logits instead of
+ *     fusing them (vp_lmhead_logits, vp_logits_ce_stats, vp_ce_max,
+ *     vp_logits_ce_bwd; at the end of this header).
  * Method: MiniMind-Tron "5 Vocab Parallelism" (sections 5.1-5.3.3) and the
- * interview note "Vocab parallelism" (Figures 1-2, key formulas, backward).
+ * interview note "Vocab parallelism" (Figures 1-2, key formulas, backward,
+ * padding).
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless the argument says "host".
