@@ -215,11 +215,11 @@ __global__ __launch_bounds__(kSegThreads) void segment_sum_kernel(
     const int64_t b = blockIdx.x;
     const int64_t p0 = b * kSegRows, p1 = min(p0 + kSegRows, n);
     const int rows = (int)(p1 - p0);
-    if (t < kSegRows + 2) {
-        const int64_t p = p0 - 1 + t;
-        sk[t] = (p >= 0 && p < n) ? keys[p] : vs;
+    for (int i = t; i < kSegRows + 2; i += kSegThreads) {
+        const int64_t p = p0 - 1 + i;
+        sk[i] = (p >= 0 && p < n) ? keys[p] : vs;
     }
-    if (t < rows) sv[t] = vals[p0 + t];
+    for (int i = t; i < rows; i += kSegThreads) sv[i] = vals[p0 + i];
     __syncthreads();
     if (sk[1] == vs) return;   // only off-shard tokens from here on
     const int64_t col = (int64_t)blockIdx.y * kSegCols + 8 * t;
