@@ -495,6 +495,10 @@ def comparator_bench(torch, vp, dev, stream, args, x_d, w0, y_d, m, s, zy, loss,
         parts = [float(np.mean([mk[i].elapsed_time(mk[i + 1]) for mk in marks])) for i in range(3)]
         out["two_pass" if two_pass else "one_read"] = {
             "ms": sum(parts), "fwd_ms": parts[0], "combine_ms": parts[1], "bwd_ms": parts[2]}
+    flops = 6.0 * N * Vs * H   # same algorithmic count as the fused path's roofline
+    for k in ("one_read", "two_pass"):
+        tf = flops / (out[k]["ms"] * 1e-3) / 1e12
+        out[k].update({"achieved_tflops": tf, "frac": tf / PEAK_BF16_TFLOPS})
     logits_bytes = logits.numel() * 4
     out.update({
         "fused_ms": fused_ms, "fused_fwd_ms": fused_avg["fwd"], "fused_bwd_ms": fused_avg["bwd"],
@@ -536,7 +540,9 @@ def padding_bench(torch, vp, dev, stream, args, x_d, w_full, y_d, m, s, zy, loss
     b.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / args.steps
+    tf = 6.0 * N * vs * H / (ms * 1e-3) / 1e12
     return {"V": 128256, "V_pad": V_pad, "shard_rows": 16032, "padded_shard_rows": vs,
+            "padded_achieved_tflops": tf, "padded_frac": tf / PEAK_BF16_TFLOPS,
             "unpadded_ms": unpadded_ms, "padded_ms": ms,
             "padded_over_unpadded": ms / unpadded_ms,
             "note": "same 63 vocabulary tiles either way: the kernels mask the shard's tail "
