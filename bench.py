@@ -142,6 +142,47 @@ def reduce_pmc(fetch_csv, write_csv, cmd_fetch, cmd_write):
     print("\n".join(lines))
 
 
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "mfma_util_shard_8b.txt")
+MFMA_COUNTERS = "GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA"
+
+
+def reduce_mfma(path, cmd):
+    """Summarise one counter run of this script (MFMA_COUNTERS with --kernel-trace) into
+    MFMA_PROFILE: per GEMM kernel, its duration, the clock it ran at (GRBM_GUI_ACTIVE is
+    summed over the 8 XCDs) and the share of SIMD cycles the MFMA unit was busy
+    (SQ_VALU_MFMA_BUSY_CYCLES summed over 1024 SIMDs), for ours and the vendor GEMM."""
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        k = int(r["Dispatch_Id"])
+        e = acc.setdefault(k, {"name": short_kernel_name(r["Kernel_Name"]),
+                               "grid": r.get("Grid_Size", r.get("Grid_Size_X", "")),
+                               "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    rows = {}
+    for k in sorted(acc):
+        e = acc[k]
+        if e.get("SQ_INSTS_MFMA", 0) == 0:
+            continue
+        cyc = e["GRBM_GUI_ACTIVE"] / 8
+        rows.setdefault((e["name"], e["grid"]), []).append(
+            (e["us"], cyc / e["us"] / 1e3, e["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / cyc))
+    lines = ["# MFMA utilisation and clock of every GEMM kernel in one bench run (rocprofv3 counters)",
+             "# command (from the repository root):", f"#   {cmd}",
+             f"#   python3 bench.py --reduce-mfma <counter csv>   (writes this file)",
+             "# clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /",
+             "# 1024 SIMDs / (GRBM_GUI_ACTIVE / 8).  Durations are under the profiler (counters on).",
+             "# The Cijk_* kernels are hipBLASLt's (torch.matmul yardsticks at the same shapes).",
+             f"kernel_source_hash: {kernel_source_hash()}", "",
+             "dispatches  avg_us  clock_GHz  mfma_busy  kernel [grid]"]
+    for (name, grid), v in rows.items():
+        n = len(v)
+        us, ghz, busy = (sum(x[i] for x in v) / n for i in range(3))
+        lines.append(f"{n:10d} {us:7.1f} {ghz:10.2f} {busy * 100:9.1f}%  {name[:70]} [{grid}]")
+    with open(MFMA_PROFILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def dev_bf16(torch, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
@@ -188,10 +229,19 @@ def main():
     ap.add_argument("--no-embed-bench", action="store_true")
     ap.add_argument("--no-yardsticks", action="store_true")
     ap.add_argument("--no-comparator", action="store_true")
+    ap.add_argument("--reduce-mfma", metavar="COUNTER_CSV",
+                    help="summarise a rocprofv3 --pmc run of this script with MFMA_COUNTERS and "
+                         "--kernel-trace into profiles/ and exit (no GPU needed)")
     ap.add_argument("--reduce-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script into profiles/ and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.reduce_mfma:
+        reduce_mfma(args.reduce_mfma,
+                    f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv -d "
+                    "gpurun_out/pmc_mfma -o run -- python3 bench.py --steps 3 --warmup 1 "
+                    "--no-cpu-baseline --no-embed-bench --no-comparator")
+        return
     if args.reduce_pmc:
         base = "rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{d} -o run -- " \
                "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-embed-bench " \
