@@ -183,6 +183,14 @@ def reduce_mfma(path, cmd):
     print("\n".join(lines))
 
 
+def device_info(torch, dev):
+    """The device and software versions the numbers were taken on."""
+    p = torch.cuda.get_device_properties(dev)
+    return {"device": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count, "hbm_GiB": round(p.total_memory / 2**30, 1),
+            "hip": torch.version.hip, "torch": torch.__version__}
+
+
 def dev_bf16(torch, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
@@ -349,6 +357,9 @@ def main():
     avg = {c: float(np.mean([mk[i].elapsed_time(mk[i + 1]) for mk in marks]))
            for i, c in enumerate(calls)}
     ce_ms = avg["fwd"] + avg["combine"] + avg["bwd"]
+    per_step = np.array([mk[0].elapsed_time(mk[4]) for mk in marks])
+    step_stats = {"median_ms": float(np.median(per_step)), "min_ms": float(per_step.min()),
+                  "p90_ms": float(np.percentile(per_step, 90)), "steps": int(per_step.size)}
     alg_flops = 6.0 * N * Vs * H
     achieved = alg_flops / (ce_ms * 1e-3) / 1e12
     exec_tflops = 8.0 * N * Vs * H / (ce_ms * 1e-3) / 1e12
@@ -406,6 +417,8 @@ def main():
                      "traffic": recorded_traffic(), "algorithmic_flops_per_launch": alg_flops,
                      "avg_launch_ms": ce_ms},
         "breakdown": breakdown,
+        "step_stats": step_stats,
+        "env": device_info(torch, dev),
         "parity": parity,
         **extra,
     }
