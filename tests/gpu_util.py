@@ -6,6 +6,11 @@ Tolerances (floating point; see the design doc for their derivation):
   dX, dW                     max|gpu - oracle| / max|oracle| <= 1e-2 per tensor
   shard statistics m, zy     max abs error <= 2e-3;  s: max relative error <= 2e-3
 Integer / byte work (the embedding) is compared bit for bit.
+
+The lookup gradient: each element is dw0 plus an fp32 sum of the bf16 gradient values
+of the L tokens that own the row (exact in fp32 once widened), so in any summation
+order |gpu - exact| <= (L + 1) 2^-24 (sum |x| + |dw0|), the recursive-summation bound
+with one more rounding for the addition to dw0.
 """
 from __future__ import annotations
 
@@ -13,11 +18,13 @@ import numpy as np
 import torch
 
 import oracle
+import vp_inputs
 
 LOSS_ATOL = 2e-3
 GRAD_RTOL = 1e-2
 STAT_ATOL = 2e-3
 STAT_RTOL = 2e-3
+U = 2.0 ** -24       # fp32 unit roundoff
 
 
 def log(msg: str) -> None:
@@ -101,6 +108,7 @@ def run_ce_path(vp, x_d, w_shards_d, starts, ends, tgt_d, grad_scale, bwd_shards
 def sampled_grads(out, t, x, w_shard, y, lse_ref, start, g, rng, k_rows=24, k_cols=24):
     """Compare sampled rows of dX_t and dW_t with the oracle evaluated on those rows."""
     n, vs = x.shape[0], w_shard.shape[0]
+    k_rows, k_cols = min(k_rows, n), min(k_cols, vs)
     rows = np.unique(np.concatenate([rng.choice(n, k_rows, replace=False), [0, n - 1]]))
     dzr = oracle.dz_rows(x[rows], w_shard, y[rows], lse_ref[rows], start, g)
     assert_grad_close(host(out["grads"][t][0][rows]), dzr @ w_shard, f"dX_{t} ({rows.size} rows)")
@@ -110,3 +118,48 @@ def sampled_grads(out, t, x, w_shard, y, lse_ref, start, g, rng, k_rows=24, k_co
                                      own[:8]])).astype(np.int64)
     dzc = oracle.dz_cols(x, w_shard[cols], cols + start, y, lse_ref, g)
     assert_grad_close(host(out["grads"][t][1][cols]), dzc.T @ x, f"dW_{t} ({cols.size} rows)")
+
+
+def embed_bwd_run(vp, ids, dout_bits, lo, hi, dw0):
+    """vp_embed_bwd on the GPU, adding into a device copy of dw0."""
+    dw = torch.from_numpy(np.ascontiguousarray(dw0, dtype=np.float32)).cuda()
+    vp.vp_embed_bwd(dev_i64(ids), dev_bf16(dout_bits), lo, hi, dw)
+    torch.cuda.synchronize()
+    return dw
+
+
+def embed_bwd_compare(got, base, want_sum, mag_sum, count, label):
+    """got = base + the row sums, within the summation bound; rows with count 0 unchanged."""
+    want = base.astype(np.float64) + want_sum
+    bound = (count[:, None] + 1.0) * U * (np.abs(base).astype(np.float64) + mag_sum)
+    err = np.abs(got - want)
+    worst = float((err - bound).max())
+    log(f"  {label}: {len(count)} rows, max abs err {err.max():.3e}, rel {rel_max(got, want):.3e}, "
+        f"longest row {int(count.max()) if count.size else 0} tokens")
+    assert worst <= 0.0, f"{label}: error above the summation bound by {worst:.3e}"
+    assert rel_max(got, want) <= 1e-2
+    untouched = count == 0
+    assert np.array_equal(got[untouched], base[untouched].astype(np.float64)), \
+        f"{label}: a row no owned id names was modified"
+
+
+def embed_bwd_assert_rows(got, dw0, ids, dout, lo, rows, label):
+    """Rows `rows` (local) of the result against dw0 + the oracle's row sums."""
+    ids = np.asarray(ids, dtype=np.int64)
+    count = np.array([(ids == lo + int(r)).sum() for r in rows], dtype=np.float64)
+    embed_bwd_compare(got, dw0[rows], oracle.embed_shard_grad_rows(ids, dout, lo, rows),
+                      oracle.embed_shard_grad_rows(ids, np.abs(dout), lo, rows), count, label)
+
+
+def embed_bwd_full_check(vp, ids, dout_bits, lo, hi, dw0=None, label=""):
+    """Every row of the shard against dw0 + the oracle's scatter-add."""
+    n, h = dout_bits.shape
+    ids = np.asarray(ids, dtype=np.int64)
+    dw0 = np.zeros((hi - lo, h), np.float32) if dw0 is None else dw0
+    got = host(embed_bwd_run(vp, ids, dout_bits, lo, hi, dw0))
+    dout = vp_inputs.bf16_bits_to_f64(dout_bits)
+    own = (ids >= lo) & (ids < hi)
+    count = np.bincount(ids[own] - lo, minlength=hi - lo).astype(np.float64)
+    embed_bwd_compare(got, dw0, oracle.embed_shard_grad(ids, dout, lo, hi),
+                      oracle.embed_shard_grad(ids, np.abs(dout), lo, hi), count, label)
+    return got

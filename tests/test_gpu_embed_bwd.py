@@ -19,11 +19,10 @@ import pytest
 
 import oracle
 import vp_inputs
-from gpu_util import dev_bf16, dev_i64, host, log, rel_max
+from gpu_util import (U, dev_bf16, dev_i64, embed_bwd_assert_rows, embed_bwd_full_check,
+                      embed_bwd_run, host, log)
 
 pytestmark = pytest.mark.gpu
-
-U = 2.0 ** -24
 
 
 @pytest.fixture(scope="module")
@@ -33,51 +32,6 @@ def vp():
         pytest.skip("no GPU")
     import vocab_lm_head_amd
     return vocab_lm_head_amd
-
-
-def _run(vp, ids, dout_bits, lo, hi, dw0):
-    import torch
-    dw = torch.from_numpy(np.ascontiguousarray(dw0, dtype=np.float32)).cuda()
-    vp.vp_embed_bwd(dev_i64(ids), dev_bf16(dout_bits), lo, hi, dw)
-    torch.cuda.synchronize()
-    return dw
-
-
-def _compare(got, base, want_sum, mag_sum, count, label):
-    """got = base + the row sums, within the summation bound; rows with count 0 unchanged."""
-    want = base.astype(np.float64) + want_sum
-    bound = (count[:, None] + 1.0) * U * (np.abs(base).astype(np.float64) + mag_sum)
-    err = np.abs(got - want)
-    worst = float((err - bound).max())
-    log(f"  {label}: {len(count)} rows, max abs err {err.max():.3e}, rel {rel_max(got, want):.3e}, "
-        f"longest row {int(count.max()) if count.size else 0} tokens")
-    assert worst <= 0.0, f"{label}: error above the summation bound by {worst:.3e}"
-    assert rel_max(got, want) <= 1e-2
-    untouched = count == 0
-    assert np.array_equal(got[untouched], base[untouched].astype(np.float64)), \
-        f"{label}: a row no owned id names was modified"
-
-
-def _assert_rows(got, dw0, ids, dout, lo, rows, label):
-    """Rows `rows` (local) of the result against dw0 + the oracle's row sums."""
-    ids = np.asarray(ids, dtype=np.int64)
-    count = np.array([(ids == lo + int(r)).sum() for r in rows], dtype=np.float64)
-    _compare(got, dw0[rows], oracle.embed_shard_grad_rows(ids, dout, lo, rows),
-             oracle.embed_shard_grad_rows(ids, np.abs(dout), lo, rows), count, label)
-
-
-def _full_check(vp, ids, dout_bits, lo, hi, dw0=None, label=""):
-    """Every row of the shard against dw0 + the oracle's scatter-add."""
-    n, h = dout_bits.shape
-    ids = np.asarray(ids, dtype=np.int64)
-    dw0 = np.zeros((hi - lo, h), np.float32) if dw0 is None else dw0
-    got = host(_run(vp, ids, dout_bits, lo, hi, dw0))
-    dout = vp_inputs.bf16_bits_to_f64(dout_bits)
-    own = (ids >= lo) & (ids < hi)
-    count = np.bincount(ids[own] - lo, minlength=hi - lo).astype(np.float64)
-    _compare(got, dw0, oracle.embed_shard_grad(ids, dout, lo, hi),
-             oracle.embed_shard_grad(ids, np.abs(dout), lo, hi), count, label)
-    return got
 
 
 def _dout(seed, n, h, scale=1.0):
@@ -93,7 +47,7 @@ def test_worked_example_backwards(vp):
     dout = _dout(0, 2, wl.embed_H)
     for t in range(wl.embed_T):
         lo, hi = vp.vp_shard_range(wl.embed_V, wl.embed_T, t)
-        got = host(_run(vp, inp.ids, dout, lo, hi, np.zeros((hi - lo, wl.embed_H), np.float32)))
+        got = host(embed_bwd_run(vp, inp.ids, dout, lo, hi, np.zeros((hi - lo, wl.embed_H), np.float32)))
         want = oracle.embed_shard_grad(inp.ids, vp_inputs.bf16_bits_to_f64(dout), lo, hi)
         assert np.array_equal(got, want), t
 
@@ -105,7 +59,7 @@ def test_small_lm_tied_ids(vp):
     dout = vp_inputs.make_embed_output_grad("small_lm")
     for t in range(wl.embed_T):
         lo, hi = vp.vp_shard_range(wl.embed_V, wl.embed_T, t)
-        _full_check(vp, inp.ids, dout, lo, hi, label=f"small_lm shard {t}")
+        embed_bwd_full_check(vp, inp.ids, dout, lo, hi, label=f"small_lm shard {t}")
 
 
 def test_accumulates_and_is_deterministic(vp):
@@ -116,8 +70,8 @@ def test_accumulates_and_is_deterministic(vp):
     ids = np.minimum(r.zipf(1.2, n) + 990, 2000).astype(np.int64)
     dout = _dout(6, n, h)
     dw0 = r.standard_normal((hi - lo, h)).astype(np.float32)
-    a = _full_check(vp, ids, dout, lo, hi, dw0, "prefilled, Zipf ids")
-    b = host(_run(vp, ids, dout, lo, hi, dw0))
+    a = embed_bwd_full_check(vp, ids, dout, lo, hi, dw0, "prefilled, Zipf ids")
+    b = host(embed_bwd_run(vp, ids, dout, lo, hi, dw0))
     assert np.array_equal(a, b), "two calls differ"
 
 
@@ -152,7 +106,7 @@ def test_edges(vp, case):
     dout = _dout(7, n, h)
     dw0 = r.standard_normal((hi - lo, h)).astype(np.float32)
     log(f"  case {case}: n={n} h={h} rows={hi - lo}")
-    _full_check(vp, ids, dout, lo, hi, dw0, case)
+    embed_bwd_full_check(vp, ids, dout, lo, hi, dw0, case)
 
 
 def test_embedding_heavy_backward(vp):
@@ -181,7 +135,7 @@ def test_embedding_heavy_backward(vp):
     # a row depends only on its own tokens: hand the oracle just those
     sub = own & np.isin(ids - lo, pick)
     dw0 = np.zeros((hi - lo, wl.embed_H), np.float32)
-    _assert_rows(got, dw0, ids[sub], vp_inputs.bf16_bits_to_f64(dout[sub]), lo, pick,
+    embed_bwd_assert_rows(got, dw0, ids[sub], vp_inputs.bf16_bits_to_f64(dout[sub]), lo, pick,
                  "embedding-heavy sampled rows")
     dout_f = vp_inputs.bf16_bits_to_f64(dout[own])
     col_gpu = dw.double().sum(dim=0).cpu().numpy()
