@@ -139,7 +139,7 @@ def test_embed_bwd_validation_and_workspace(lib):
     ws = lib.vp_embed_bwd_workspace
     n, h, vs = 65536, 4096, 64000
     r256 = lambda b: -(-b // 256) * 256
-    nblk, nseg = -(-n // 1024), -(-n // 32)     # radix-sort tiles, segment-sum blocks
+    nblk, nseg = -(-n // 1024), -(-n // 64)     # radix-sort tiles, segment-sum blocks
     need = ws(n, h, 0, vs)
     assert need == 4 * r256(4 * n) + r256(256 * nblk * 4) + 2 * r256(nseg * h * 4)
     assert ws(0, h, 0, vs) == 0 and ws(n, 12, 0, vs) == 0 and ws(n, h, 5, 5) == 0

@@ -20,6 +20,8 @@
 //   3. segment_fixup_kernel: the block where such a row starts adds its pieces in
 //      block order and adds the total to dw.
 // Each row of dw is read and written once, by one workgroup per column block.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -36,10 +38,11 @@ constexpr int kSortTile = kSortThreads * kSortRounds;  // elements per workgroup
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kSortSegs = kSortRounds * kSortWaves;    // (round, wave) groups, in element order
 
-constexpr int kSegRows = 32;        // sorted positions per segment-sum block
+constexpr int kSegRows = 64;        // sorted positions per segment-sum block
 constexpr int kSegThreads = 64;     // one wave
 constexpr int kSegCols = 8 * kSegThreads;   // columns per block (8 bf16 = 16 bytes per thread)
-constexpr int kSegBatch = 8;        // dout rows (and the dw rows they finish) in flight per thread
+constexpr int kSegBatch = 16;       // dout rows (and the dw rows they finish) in flight per thread
+constexpr int64_t kSegMaxGrid = 1 << 20;   // segment-sum workgroups per launch (grid-stride beyond)
 
 // Sort key of element e: in the first pass it is made from the id, later passes
 // read the previous pass's output.
@@ -205,14 +208,12 @@ __device__ __forceinline__ void store_row(float *dst, const float (&acc)[8]) {
 // row, and how, follows from the keys alone (sorted: the row began before the block
 // exactly when its key equals the key just before the block), so each batch issues the
 // loads of its dout rows and of the dw rows it finishes together.
-__global__ __launch_bounds__(kSegThreads) void segment_sum_kernel(
-    const uint32_t *__restrict__ keys, const uint32_t *__restrict__ vals, int64_t n, uint32_t vs,
-    const uint16_t *__restrict__ dout, int64_t h, float *__restrict__ dw,
-    float *__restrict__ part_first, float *__restrict__ part_last) {
-    __shared__ uint32_t sk[kSegRows + 2];   // keys p0-1 .. p1 (vs where outside [0, n))
-    __shared__ uint32_t sv[kSegRows];
+// sk holds the keys of positions p0-1 .. p1 (vs where outside [0, n)), sv the tokens.
+__device__ __forceinline__ void segment_block(
+    int64_t b, int64_t cb, const uint32_t *__restrict__ keys, const uint32_t *__restrict__ vals,
+    int64_t n, uint32_t vs, const uint16_t *__restrict__ dout, int64_t h, float *__restrict__ dw,
+    float *__restrict__ part_first, float *__restrict__ part_last, uint32_t *sk, uint32_t *sv) {
     const int t = threadIdx.x;
-    const int64_t b = blockIdx.x;
     const int64_t p0 = b * kSegRows, p1 = min(p0 + kSegRows, n);
     const int rows = (int)(p1 - p0);
     for (int i = t; i < kSegRows + 2; i += kSegThreads) {
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kSegThreads) void segment_sum_kernel(
     for (int i = t; i < rows; i += kSegThreads) sv[i] = vals[p0 + i];
     __syncthreads();
     if (sk[1] == vs) return;   // only off-shard tokens from here on
-    const int64_t col = (int64_t)blockIdx.y * kSegCols + 8 * t;
+    const int64_t col = cb * kSegCols + 8 * t;
     const bool active = col < h;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int q0 = 0; q0 < rows; q0 += kSegBatch) {
@@ -266,6 +267,23 @@ __global__ __launch_bounds__(kSegThreads) void segment_sum_kernel(
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[c] = 0.f;
         }
+    }
+}
+
+// One wave per (block of sorted positions, column block), the column block varying
+// fastest: owned keys sort first, so the blocks with work are the first ones dispatched
+// and run side by side, instead of each column block's few active waves being spread
+// among the many that find only off-shard keys and return.  Grid-stride beyond the grid.
+__global__ __launch_bounds__(kSegThreads) void segment_sum_kernel(
+    const uint32_t *__restrict__ keys, const uint32_t *__restrict__ vals, int64_t n, uint32_t vs,
+    const uint16_t *__restrict__ dout, int64_t h, float *__restrict__ dw,
+    float *__restrict__ part_first, float *__restrict__ part_last, int64_t ncb, int64_t total) {
+    __shared__ uint32_t sk[kSegRows + 2];
+    __shared__ uint32_t sv[kSegRows];
+    for (int64_t id = blockIdx.x; id < total; id += gridDim.x) {
+        segment_block(id / ncb, id % ncb, keys, vals, n, vs, dout, h, dw, part_first, part_last,
+                      sk, sv);
+        __syncthreads();   // sk and sv are restaged by the next block
     }
 }
 
@@ -370,9 +388,10 @@ hipError_t launch_embed_bwd(const int64_t *ids, int64_t n, const uint16_t *dout,
     }
     const uint32_t *sk = keys[(passes - 1) & 1], *sv = vals[(passes - 1) & 1];
     float *first = (float *)(base + w.off_first), *last = (float *)(base + w.off_last);
-    const dim3 grid((unsigned)w.nseg, (unsigned)ceil_div(h, kSegCols));
-    hipLaunchKernelGGL(segment_sum_kernel, grid, dim3(kSegThreads), 0, stream, sk, sv, n,
-                       (uint32_t)vs, dout, h, dw, first, last);
+    const int64_t ncb = ceil_div(h, kSegCols), total = w.nseg * ncb;
+    hipLaunchKernelGGL(segment_sum_kernel, dim3((unsigned)std::min<int64_t>(total, kSegMaxGrid)),
+                       dim3(kSegThreads), 0, stream, sk, sv, n, (uint32_t)vs, dout, h, dw, first,
+                       last, ncb, total);
     hipLaunchKernelGGL(segment_fixup_kernel, dim3((unsigned)w.nseg), dim3(kFixThreads), 0, stream, sk,
                        n, (uint32_t)vs, h, dw, first, last);
     return hipGetLastError();
