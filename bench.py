@@ -27,7 +27,6 @@ from __future__ import annotations
 
 import argparse
 import csv
-import glob
 import hashlib
 import json
 import os
@@ -53,10 +52,16 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# the sources the CE sequence's kernels are compiled from (and the build flags)
+CE_SOURCES = ("common.hpp", "gemm.hpp", "launch.hpp", "ce_fwd.hip", "ce_combine.hip", "ce_bwd.hip")
+
+
 def kernel_source_hash() -> str:
-    """Hash of everything that decides the kernels' code: sources and build flags."""
+    """Hash of everything that decides the CE sequence's kernel code: its sources and the
+    build script (flags).  The counter summaries record it, so that a reading taken on
+    other kernels is never reported."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "vocab_lm_head_amd", "csrc", "*")))
+    files = [os.path.join(ROOT, "vocab_lm_head_amd", "csrc", f) for f in CE_SOURCES]
     files.append(os.path.join(ROOT, "vocab_lm_head_amd", "build.py"))
     for f in files:
         h.update(os.path.basename(f).encode())
