@@ -249,23 +249,23 @@ def main():
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script into profiles/ and exit (no GPU needed)")
     args = ap.parse_args()
+    # the counter runs' commands, as recorded in the summaries: the output folder is the
+    # one the given CSV files were written to (rocprofv3 -d <folder> -o run)
+    run_args = "-o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline " \
+               "--no-embed-bench --no-comparator"
     if args.reduce_mfma:
         reduce_mfma(args.reduce_mfma,
                     f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv -d "
-                    "gpurun_out/pmc_mfma -o run -- python3 bench.py --steps 3 --warmup 1 "
-                    "--no-cpu-baseline --no-embed-bench --no-comparator")
+                    f"{os.path.dirname(args.reduce_mfma)} {run_args}")
         return
     if args.reduce_pmc:
-        base = "rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{d} -o run -- " \
-               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-embed-bench " \
-               "--no-comparator"
-        reduce_pmc(args.reduce_pmc[0], args.reduce_pmc[1], base.format(c="FETCH_SIZE", d="fetch"),
-                   base.format(c="WRITE_SIZE", d="write"))
+        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {os.path.dirname(path)} {run_args}"
+                for c, path in zip(("FETCH_SIZE", "WRITE_SIZE"), args.reduce_pmc)]
+        reduce_pmc(args.reduce_pmc[0], args.reduce_pmc[1], cmds[0], cmds[1])
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(vocab shards would map one per GPU; see DESIGN.md). Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (each vocab "
+              "shard would run on a GPU of its own). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,7 +1,7 @@
 """Helpers of the GPU parity tests: moving input bits to the device, running the
 HIP path through the C ABI binding, and the comparison bars.
 
-Tolerances (floating point; see the design doc for their derivation):
+Tolerances (floating point):
   per-token loss and lse     max abs error <= 2e-3
   dX, dW                     max|gpu - oracle| / max|oracle| <= 1e-2 per tensor
   shard statistics m, zy     max abs error <= 2e-3;  s: max relative error <= 2e-3

@@ -11,7 +11,7 @@ scaled, then rounded to bf16 with round-to-nearest-even and returned as
 ``uint16`` bit patterns; both sides widen those same bits.
 
 Workloads (sizes and distributions as the five workload descriptions give
-them; every reading of an unstated detail is listed in the design doc):
+them; where those leave a detail open, the choice is stated beside it):
 
 * ``tiny``              N=6, H=32, V=16, T=4, logits std ~5; plus the V=8, T=2
                         embedding example with ids [1, 6].
