@@ -212,6 +212,10 @@ def vp_ce_combine(m, s, zy, targets, ignore_index: int = DEFAULT_IGNORE_INDEX,
     loss = torch.empty(n, dtype=torch.float32, device=dev) if loss is None else loss
     lse = torch.empty(n, dtype=torch.float32, device=dev) if lse is None else lse
     loss_mean = torch.empty(1, dtype=torch.float32, device=dev) if loss_mean is None else loss_mean
+    for t, nm, size in ((loss, "loss", n), (lse, "lse", n), (loss_mean, "loss_mean", 1)):
+        _need(t, torch.float32, 1, nm)
+        if t.shape[0] != size:
+            raise ValueError(f"{nm} must have {size} elements")
     _check(lib.vp_ce_combine(_ptr(m), _ptr(s), _ptr(zy), _ptr(targets), n, T, int(ignore_index),
                              _ptr(loss), _ptr(lse), _ptr(loss_mean), _stream(stream)),
            "vp_ce_combine")
