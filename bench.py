@@ -20,8 +20,9 @@ in HBM instead of fused (the pages' tensor-parallel baseline; --no-comparator sk
 it); and, unless --no-embed-bench, the step's CE sequence on
 the padded vocabulary (shard 0 = 16128 rows instead of 16032), the embedding-heavy
 lookup (65536 Zipf ids on a [64000, 4096] shard) and its weight gradient, each
-against HBM bandwidth; and yardsticks (vendor GEMM, copy, fill) unless
---no-yardsticks.
+against HBM bandwidth; the same CE sequence at the large-vocab shard and at the
+embedding-heavy T=1 cross entropy unless --no-other-workloads; and yardsticks (vendor
+GEMM, copy, fill) unless --no-yardsticks.
 """
 from __future__ import annotations
 
@@ -242,6 +243,8 @@ def main():
     ap.add_argument("--no-embed-bench", action="store_true")
     ap.add_argument("--no-yardsticks", action="store_true")
     ap.add_argument("--no-comparator", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the large-vocab and embedding-heavy CE timings")
     ap.add_argument("--reduce-mfma", metavar="COUNTER_CSV",
                     help="summarise a rocprofv3 --pmc run of this script with MFMA_COUNTERS and "
                          "--kernel-trace into profiles/ and exit (no GPU needed)")
@@ -252,7 +255,7 @@ def main():
     # the counter runs' commands, as recorded in the summaries: the output folder is the
     # one the given CSV files were written to (rocprofv3 -d <folder> -o run)
     run_args = "-o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline " \
-               "--no-embed-bench --no-comparator"
+               "--no-embed-bench --no-comparator --no-other-workloads"
     if args.reduce_mfma:
         reduce_mfma(args.reduce_mfma,
                     f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv -d "
@@ -395,6 +398,12 @@ def main():
         extra["embedding_heavy_lookup"] = embed_bench(torch, vp, vp_inputs, dev, stream, args)
         extra["embedding_heavy_backward"] = embed_bwd_bench(torch, vp, vp_inputs, dev, stream, args,
                                                             keep=embed_inputs)
+    if not args.no_other_workloads:
+        extra["other_workloads"] = {}
+        for name in ("large_vocab", "embedding_heavy"):
+            extra["other_workloads"][name] = ce_workload_bench(torch, vp, vp_inputs, dev, stream,
+                                                               args, name)
+            torch.cuda.empty_cache()
     if not args.no_yardsticks:
         extra["yardsticks"] = yardsticks(torch, dev, stream, N, H, Vs)
 
@@ -469,6 +478,69 @@ def yardsticks(torch, dev, stream, N, H, Vs, reps=10):
     out["copy_GBs"] = 2 * a.numel() * 2 / (ms * 1e-3) / 1e9
     ms = timed(lambda: a.fill_(1))
     out["fill_GBs"] = a.numel() * 2 / (ms * 1e-3) / 1e9
+    return out
+
+
+def ce_workload_bench(torch, vp, vp_inputs, dev, stream, args, name):
+    """The fused CE sequence of shard 0 (forward, combine over the T shards, backward) at
+    another workload: the large-vocab shard (N=16384, H=8192, shard [19008, 8192], T=8,
+    shards 1-7 given as synthetic statistics) or the embedding-heavy T=1 cross entropy
+    (N=4096, H=4096, V=256000).  Gated on every token's loss against the oracle golden;
+    the same algorithmic count (6 N Vs H) and peak as the headline roofline."""
+    inp = vp_inputs.make_inputs(name)
+    wl = inp.wl
+    N, H, T, Vs = wl.N, wl.H, wl.T, wl.Vs
+    x_d = dev_bf16(torch, inp.x, dev)
+    w0 = dev_bf16(torch, inp.w_shard(0), dev)
+    y = inp.targets
+    y_d = torch.from_numpy(y).to(dev)
+    m = torch.empty((T, N), dtype=torch.float32, device=dev)
+    s, zy = torch.empty_like(m), torch.empty_like(m)
+    if T > 1:   # the other shards' statistics (other GPUs' work), made up
+        ms, ss, zs = vp_inputs.synthetic_triples(name, y)
+        m[1:].copy_(torch.from_numpy(ms[1:]))
+        s[1:].copy_(torch.from_numpy(ss[1:]))
+        zy[1:].copy_(torch.from_numpy(zs[1:]))
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    lse, mean = torch.empty_like(loss), torch.empty(1, dtype=torch.float32, device=dev)
+    dx = torch.empty((N, H), dtype=torch.float32, device=dev)
+    dw = torch.empty((Vs, H), dtype=torch.float32, device=dev)
+    ws_f = vp.alloc_workspace(vp.vp_lmhead_ce_fwd_workspace(N, H, 0, Vs), dev)
+    ws_b = vp.alloc_workspace(vp.vp_lmhead_ce_bwd_workspace(N, H, 0, Vs), dev)
+    g = 1.0 / max(1, int((y != vp.DEFAULT_IGNORE_INDEX).sum()))
+
+    def step(marks=None):
+        if marks:
+            marks[0].record(stream)
+        vp.vp_lmhead_ce_fwd(x_d, w0, y_d, 0, Vs, m[0], s[0], zy[0], workspace=ws_f)
+        vp.vp_ce_combine(m, s, zy, y_d, loss=loss, lse=lse, loss_mean=mean)
+        vp.vp_lmhead_ce_bwd(x_d, w0, y_d, lse, 0, Vs, g, dx=dx, dw=dw, workspace=ws_b)
+        if marks:
+            marks[1].record(stream)
+
+    step()
+    torch.cuda.synchronize()
+    gold = np.load(os.path.join(ROOT, "tests", "golden", f"oracle_{name}.npz"))
+    lerr = float(np.abs(loss.cpu().double().numpy() - gold["loss"]).max())
+    out = {"workload": f"{name}: N={N}, H={H}, V={wl.V}, T={T}, shard 0 = [{Vs}, {H}] bf16",
+           "parity": {"loss_max_abs_err": lerr, "bar": 2e-3}}
+    if not lerr <= 2e-3:
+        out["error"] = "parity failed: no time reported"
+        return out
+    steps = max(1, min(args.steps, 10))
+    for _ in range(min(args.warmup, 3)):
+        step()
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        step(marks[k])
+    torch.cuda.synchronize()
+    t = np.array([mk[0].elapsed_time(mk[1]) for mk in marks])
+    ms = float(np.median(t))
+    tf = 6.0 * N * Vs * H / (ms * 1e-3) / 1e12
+    out.update({"median_ms": ms, "min_ms": float(t.min()), "steps": steps,
+                "tokens_per_s": N / (ms * 1e-3), "achieved_tflops": tf,
+                "frac": tf / PEAK_BF16_TFLOPS, "executed_tflops": tf * 8.0 / 6.0})
     return out
 
 

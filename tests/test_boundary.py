@@ -119,6 +119,10 @@ def test_fwd_validation_and_workspace(lib):
     slices = -(-16032 // 128)
     assert need == -(-(3 * slices * 8192 * 4) // 256) * 256
     assert ws(8192, 12, 0, 16032) == 0          # invalid h -> 0
+    # few tokens over many slices: the merge splits the 2000 slices 8 ways, whose results
+    # ([3, 8, n] fp32) follow the per-slice partials
+    r256 = lambda b: -(-b // 256) * 256
+    assert ws(4096, 4096, 0, 256000) == r256(3 * 2000 * 4096 * 4) + r256(3 * 8 * 4096 * 4)
     f = lib.vp_lmhead_ce_fwd
     args = lambda **k: [k.get("x", FAKE), k.get("w", FAKE), k.get("t", FAKE), k.get("n", 8192),
                         k.get("h", 4096), k.get("lo", 0), k.get("hi", 16032), FAKE, FAKE, FAKE,

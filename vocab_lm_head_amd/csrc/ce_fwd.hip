@@ -8,6 +8,8 @@
 // shard's 128-row vocabulary slices are merged with
 //   (m, s) <- (max(m, m'), s e^(m - max) + s' e^(m' - max)),
 // which is exact in real arithmetic; the [N, Vs] logits never leave registers.
+#include <algorithm>
+
 #include "gemm.hpp"
 #include "launch.hpp"
 
@@ -109,32 +111,37 @@ struct CeStatsEpilogue {
     }
 };
 
-// Merge the shard's per-slice partials of each token.  A workgroup takes 32
-// tokens; its 8 thread groups each merge every 8th slice, kMergeBatch slices at a
-// time with all of their loads issued before the first is used, then the 8
-// partial results are merged through LDS.
+// Merge the shard's per-slice partials of each token.  A workgroup takes 32 tokens
+// and the slices [blockIdx.y chunk, (blockIdx.y + 1) chunk); its 8 thread groups each
+// merge every 8th of them, kMergeBatch slices at a time with all of their loads issued
+// before the first is used, then the 8 partial results are merged through LDS and
+// written at row blockIdx.y of the outputs (rows out_stride apart).  The input and the
+// output rows share one layout, [3][rows][n] (max, sum-exp, target logit), so the
+// same kernel merges the per-split results of a first pass.
 constexpr int kMergeTok = 32, kMergeGrp = 8, kMergeBatch = 4;
 __global__ __launch_bounds__(kMergeTok * kMergeGrp) void merge_slices_kernel(
-    const float *__restrict__ part, int64_t slices, int64_t n, float *__restrict__ m_out,
-    float *__restrict__ s_out, float *__restrict__ zy_out) {
+    const float *__restrict__ part, int64_t slices, int64_t n, int64_t chunk,
+    float *__restrict__ m_out, float *__restrict__ s_out, float *__restrict__ zy_out,
+    int64_t out_stride) {
     __shared__ float sm[kMergeGrp][kMergeTok], ss[kMergeGrp][kMergeTok], sz[kMergeGrp][kMergeTok];
     const int t = threadIdx.x % kMergeTok, g = threadIdx.x / kMergeTok;
     const int64_t i = (int64_t)blockIdx.x * kMergeTok + t;
     const int64_t ic = i < n ? i : n - 1;   // past n: a valid address, result unused
+    const int64_t p_lo = (int64_t)blockIdx.y * chunk, p_hi = min(p_lo + chunk, slices);
     float m = -INFINITY, s = 0.f, zy = 0.f;
-    for (int64_t p0 = g; p0 < slices; p0 += kMergeGrp * kMergeBatch) {
+    for (int64_t p0 = p_lo + g; p0 < p_hi; p0 += kMergeGrp * kMergeBatch) {
         float mp[kMergeBatch], sp[kMergeBatch], zp[kMergeBatch];
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
             const int64_t p = p0 + u * kMergeGrp;
-            const int64_t pc = p < slices ? p : slices - 1;
+            const int64_t pc = p < p_hi ? p : p_hi - 1;
             mp[u] = part[pc * n + ic];
             sp[u] = part[(slices + pc) * n + ic];
             zp[u] = part[(2 * slices + pc) * n + ic];
         }
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
-            if (p0 + u * kMergeGrp >= slices) break;
+            if (p0 + u * kMergeGrp >= p_hi) break;
             const float mx = fmaxf(m, mp[u]);
             s = s * fast_exp2((m - mx) * kLog2e) + sp[u] * fast_exp2((mp[u] - mx) * kLog2e);
             m = mx;
@@ -153,18 +160,37 @@ __global__ __launch_bounds__(kMergeTok * kMergeGrp) void merge_slices_kernel(
             if (ss[q][t] != 0.f) S += ss[q][t] * fast_exp2((sm[q][t] - M) * kLog2e);
             Z += sz[q][t];
         }
-        m_out[i] = M;
-        s_out[i] = S;
-        zy_out[i] = Z;
+        const int64_t o = (int64_t)blockIdx.y * out_stride + i;
+        m_out[o] = M;
+        s_out[o] = S;
+        zy_out[o] = Z;
     }
 }
+
+// The slices are split over more workgroups (a first pass whose per-split results a
+// second pass merges) when one workgroup per 32 tokens would leave most of the chip idle
+// (fewer than kMergeMinBlocks of them: aim for kMergeTargetBlocks) or would walk more
+// than kMergeMaxSlices slices each.
+constexpr int64_t kMergeMinBlocks = 256;
+constexpr int64_t kMergeTargetBlocks = 1024;
+constexpr int64_t kMergeMaxSlices = 256;
 
 }  // namespace
 
 FwdWorkspace fwd_workspace(int64_t n, int64_t vs) {
     FwdWorkspace w;
     w.slices = ceil_div(vs, kSlice);
-    w.bytes = (size_t)round_up(3 * w.slices * n * (int64_t)sizeof(float), 256);
+    const int64_t tb = ceil_div(n, kMergeTok);
+    w.splits = ceil_div(w.slices, kMergeMaxSlices);
+    if (tb > 0 && tb < kMergeMinBlocks) {
+        const int64_t most = std::max<int64_t>(1, w.slices / (kMergeGrp * kMergeBatch));
+        w.splits = std::max(w.splits, std::min(ceil_div(kMergeTargetBlocks, tb), most));
+    }
+    w.chunk = ceil_div(w.slices, w.splits);
+    w.splits = ceil_div(w.slices, w.chunk);   // no empty split
+    w.off_split = (size_t)round_up(3 * w.slices * n * (int64_t)sizeof(float), 256);
+    w.bytes = w.off_split +
+              (w.splits > 1 ? (size_t)round_up(3 * w.splits * n * (int64_t)sizeof(float), 256) : 0);
     return w;
 }
 
@@ -179,8 +205,18 @@ hipError_t launch_ce_fwd(const uint16_t *x, const uint16_t *w, const int64_t *ta
     Operand B{x, h, (int)n};
     hipLaunchKernelGGL(gemm_nt_kernel<CeStatsEpilogue>, dim3(g.blocks()), dim3(kThreads), 0, stream,
                        A, B, (int)h, g.tiles_m, g.tiles_n, epi);
-    hipLaunchKernelGGL(merge_slices_kernel, dim3((unsigned)ceil_div(n, kMergeTok)),
-                       dim3(kMergeTok * kMergeGrp), 0, stream, part, fw.slices, n, m_out, s_out, zy_out);
+    const unsigned tb = (unsigned)ceil_div(n, kMergeTok);
+    if (fw.splits == 1) {
+        hipLaunchKernelGGL(merge_slices_kernel, dim3(tb), dim3(kMergeTok * kMergeGrp), 0, stream, part,
+                           fw.slices, n, fw.slices, m_out, s_out, zy_out, (int64_t)0);
+    } else {
+        float *p2 = (float *)((char *)ws + fw.off_split);   // [3][splits][n]
+        hipLaunchKernelGGL(merge_slices_kernel, dim3(tb, (unsigned)fw.splits),
+                           dim3(kMergeTok * kMergeGrp), 0, stream, part, fw.slices, n, fw.chunk, p2,
+                           p2 + fw.splits * n, p2 + 2 * fw.splits * n, n);
+        hipLaunchKernelGGL(merge_slices_kernel, dim3(tb), dim3(kMergeTok * kMergeGrp), 0, stream, p2,
+                           fw.splits, n, fw.splits, m_out, s_out, zy_out, (int64_t)0);
+    }
     return hipGetLastError();
 }
 

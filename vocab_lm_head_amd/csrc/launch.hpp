@@ -12,7 +12,9 @@ namespace vp {
 // forward workspace: fp32 partial (max, sum-exp, target logit) per 128-row
 // vocabulary slice and token
 struct FwdWorkspace {
-    int64_t slices;        // ceil(Vs / 128)
+    int64_t slices;        // ceil(Vs / 128): per-slice partials [3][slices][n] at offset 0
+    int64_t splits, chunk; // the merge's slice splits (1: a single pass) of `chunk` slices
+    size_t off_split;      // per-split results [3][splits][n] when splits > 1
     size_t bytes;
 };
 FwdWorkspace fwd_workspace(int64_t n, int64_t vs);
