@@ -20,8 +20,8 @@ in HBM instead of fused (the pages' tensor-parallel baseline; --no-comparator sk
 it); and, unless --no-embed-bench, the step's CE sequence on
 the padded vocabulary (shard 0 = 16128 rows instead of 16032), the embedding-heavy
 lookup (65536 Zipf ids on a [64000, 4096] shard) and its weight gradient, each
-against HBM bandwidth; the same CE sequence at the large-vocab shard and at the
-embedding-heavy T=1 cross entropy unless --no-other-workloads; and yardsticks (vendor
+against HBM bandwidth; the same CE sequence at the small LM, the large-vocab shard
+and the embedding-heavy T=1 cross entropy unless --no-other-workloads; and yardsticks (vendor
 GEMM, copy, fill) unless --no-yardsticks.
 """
 from __future__ import annotations
@@ -86,7 +86,8 @@ def recorded_traffic():
 
 
 CE_KERNELS = ("CeStatsEpilogue", "merge_slices_kernel", "combine_kernel", "mean_kernel",
-              "transpose_bf16_kernel", "DlogitsEpilogue", "StoreTransposedEpilogue")
+              "transpose_bf16_kernel", "DlogitsEpilogue", "StoreTransposedEpilogue",
+              "gemm_nt_splitk_store_kernel", "sum_splits_kernel")
 
 
 def short_kernel_name(name: str) -> str:
@@ -244,7 +245,7 @@ def main():
     ap.add_argument("--no-yardsticks", action="store_true")
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
-                    help="skip the large-vocab and embedding-heavy CE timings")
+                    help="skip the small-LM, large-vocab and embedding-heavy CE timings")
     ap.add_argument("--reduce-mfma", metavar="COUNTER_CSV",
                     help="summarise a rocprofv3 --pmc run of this script with MFMA_COUNTERS and "
                          "--kernel-trace into profiles/ and exit (no GPU needed)")
@@ -400,7 +401,7 @@ def main():
                                                             keep=embed_inputs)
     if not args.no_other_workloads:
         extra["other_workloads"] = {}
-        for name in ("large_vocab", "embedding_heavy"):
+        for name in ("small_lm", "large_vocab", "embedding_heavy"):
             extra["other_workloads"][name] = ce_workload_bench(torch, vp, vp_inputs, dev, stream,
                                                                args, name)
             torch.cuda.empty_cache()
@@ -483,9 +484,10 @@ def yardsticks(torch, dev, stream, N, H, Vs, reps=10):
 
 def ce_workload_bench(torch, vp, vp_inputs, dev, stream, args, name):
     """The fused CE sequence of shard 0 (forward, combine over the T shards, backward) at
-    another workload: the large-vocab shard (N=16384, H=8192, shard [19008, 8192], T=8,
-    shards 1-7 given as synthetic statistics) or the embedding-heavy T=1 cross entropy
-    (N=4096, H=4096, V=256000).  Gated on every token's loss against the oracle golden;
+    another workload: the small LM (N=4096, H=512, V=6400, T=2; launch-bound), the
+    large-vocab shard (N=16384, H=8192, shard [19008, 8192], T=8, shards 1-7 given as
+    synthetic statistics) or the embedding-heavy T=1 cross entropy (N=4096, H=4096,
+    V=256000).  Gated on every token's loss against the oracle golden;
     the same algorithmic count (6 N Vs H) and peak as the headline roofline."""
     inp = vp_inputs.make_inputs(name)
     wl = inp.wl
@@ -496,11 +498,15 @@ def ce_workload_bench(torch, vp, vp_inputs, dev, stream, args, name):
     y_d = torch.from_numpy(y).to(dev)
     m = torch.empty((T, N), dtype=torch.float32, device=dev)
     s, zy = torch.empty_like(m), torch.empty_like(m)
-    if T > 1:   # the other shards' statistics (other GPUs' work), made up
+    if T > 1 and wl.synthetic_other_shards:   # the other shards' statistics, made up
         ms, ss, zs = vp_inputs.synthetic_triples(name, y)
         m[1:].copy_(torch.from_numpy(ms[1:]))
         s[1:].copy_(torch.from_numpy(ss[1:]))
         zy[1:].copy_(torch.from_numpy(zs[1:]))
+    elif T > 1:   # computed from their weight rows, untimed (other GPUs' work)
+        for t in range(1, T):
+            wt = dev_bf16(torch, inp.w_shard(t), dev)
+            vp.vp_lmhead_ce_fwd(x_d, wt, y_d, t * Vs, (t + 1) * Vs, m[t], s[t], zy[t])
     loss = torch.empty(N, dtype=torch.float32, device=dev)
     lse, mean = torch.empty_like(loss), torch.empty(1, dtype=torch.float32, device=dev)
     dx = torch.empty((N, H), dtype=torch.float32, device=dev)

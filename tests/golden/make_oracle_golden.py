@@ -4,7 +4,8 @@
 
 Calls only ``oracle/`` (fp64 NumPy) and the seeded input generators
 (``vp_inputs``); nothing from the HIP path.  For each workload whose dense
-logits are too large to recompute inside a GPU test, it stores per token
+logits are too large to recompute inside a GPU test (and for the small-LM workload,
+whose bench timing is gated on it), it stores per token
 
   lse   the full-vocabulary log-sum-exp (fp64)
   loss  the per-token cross entropy (fp64)
@@ -70,8 +71,14 @@ def golden_embedding_heavy():
     return _dense_chunked(_f64(inp.x), _f64(inp.w), inp.targets, chunk=256)
 
 
+def golden_small_lm():
+    """Dense cross entropy over V = 6400 (both shards) on N = 4096 tokens."""
+    inp = vp_inputs.make_inputs("small_lm")
+    return _dense_chunked(_f64(inp.x), _f64(inp.w), inp.targets, chunk=1024)
+
+
 MAKERS = {"shard_8b": golden_shard_8b, "large_vocab": golden_large_vocab,
-          "embedding_heavy": golden_embedding_heavy}
+          "embedding_heavy": golden_embedding_heavy, "small_lm": golden_small_lm}
 
 
 def main(names):

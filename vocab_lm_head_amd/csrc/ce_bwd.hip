@@ -197,6 +197,62 @@ __global__ void fill_zero_kernel(float *p, int64_t count) {
         p[i] = 0.f;
 }
 
+// Split-K form of the transposed store: the grid holds `splits` copies of the tile grid,
+// and copy s computes every tile over the K columns [s chunk, min((s + 1) chunk, K)) of
+// both operands (chunk a multiple of kBK, so the shifted rows stay 128-byte aligned) and
+// stores its partial at epi.out + s out_stride.  A reduction then sums the partials in
+// split order.  For outputs with too few tiles to fill the chip.
+__global__ __launch_bounds__(kThreads, 1) void gemm_nt_splitk_store_kernel(
+    Operand A, Operand B, int K, int chunk, int tiles_m, int tiles_n, StoreTransposedEpilogue epi,
+    int64_t out_stride) {
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * kStage];
+    const int tiles = tiles_m * tiles_n;
+    const int split = blockIdx.x / tiles;
+    const int k0 = split * chunk;
+    Operand a = A, b = B;
+    a.p += k0;
+    b.p += k0;
+    epi.out += split * out_stride;
+    gemm_nt_tile(a, b, min(chunk, K - k0), tiles_m, tiles_n, epi, blockIdx.x - split * tiles, smem);
+}
+
+// out[i] = sum over s of part[s stride + i] for i < count, in split order (fp32).  count
+// and stride are multiples of 4 and the buffers 16-byte aligned.
+constexpr int kMaxSplits = 16;
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float *__restrict__ part, int splits,
+                                                         int64_t count, int64_t stride,
+                                                         float *__restrict__ out) {
+    const f32x4 *p = (const f32x4 *)part;
+    const int64_t n4 = count / 4, s4 = stride / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        f32x4 v[kMaxSplits];
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s)
+            if (s < splits) v[s] = p[s * s4 + i];
+        f32x4 acc = v[0];
+#pragma unroll
+        for (int s = 1; s < kMaxSplits; ++s)
+            if (s < splits) acc += v[s];
+        ((f32x4 *)out)[i] = acc;
+    }
+}
+
+// K splits of a gradient GEMM with `tiles` output tiles: below one tile per CU the K
+// loop is split (aiming at kSplitTargetBlocks workgroups, at least kSplitMinSteps K
+// steps each); chunk is a multiple of kBK.
+constexpr int64_t kSplitMinTiles = 256;
+constexpr int64_t kSplitTargetBlocks = 512;
+constexpr int64_t kSplitMinSteps = 8;
+void grad_split(int64_t tiles, int64_t K, int64_t &splits, int64_t &chunk) {
+    splits = 1;
+    if (tiles < kSplitMinTiles)
+        splits = std::max<int64_t>(1, std::min({ceil_div(kSplitTargetBlocks, tiles),
+                                                K / (kBK * kSplitMinSteps), (int64_t)kMaxSplits}));
+    chunk = round_up(ceil_div(K, splits), kBK);
+    splits = ceil_div(K, chunk);
+}
+
 }  // namespace
 
 BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs) {
@@ -215,6 +271,11 @@ BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs) {
     b.off_wt = take((size_t)h * b.vs_ld * 2);
     b.off_dz = take((size_t)n * b.vs_ld * 2);
     b.off_dzt = take((size_t)vs * b.n_ld * 2);
+    grad_split(gemm_grid(h, n).blocks(), b.vs_ld, b.splits_dx, b.chunk_dx);
+    grad_split(gemm_grid(h, vs).blocks(), b.n_ld, b.splits_dw, b.chunk_dw);
+    const int64_t part = std::max(b.splits_dx > 1 ? b.splits_dx * n * h : 0,
+                                  b.splits_dw > 1 ? b.splits_dw * vs * h : 0);
+    b.off_split = take((size_t)part * 4);
     b.bytes = off;
     return b;
 }
@@ -237,21 +298,36 @@ hipError_t launch_bwd_grad_gemms(int64_t n, int64_t h, int64_t vs, float *dx, fl
     const uint16_t *wt = (const uint16_t *)(base + b.off_wt);
     const uint16_t *dz = (const uint16_t *)(base + b.off_dz);
     const uint16_t *dzt = (const uint16_t *)(base + b.off_dzt);
-    {   // dX_r^T [H, N] = W_r^T [H, Vs64] . dz [N, Vs64]^T
-        const GemmGrid g = gemm_grid(h, n);
-        StoreTransposedEpilogue epi{dx, h, (int)h, (int)n};
-        hipLaunchKernelGGL(gemm_nt_kernel<StoreTransposedEpilogue>, dim3(g.blocks()), dim3(kThreads),
-                           0, stream, Operand{wt, b.vs_ld, (int)h}, Operand{dz, b.vs_ld, (int)n},
-                           (int)b.vs_ld, g.tiles_m, g.tiles_n, epi);
-    }
-    {   // dW_r^T [H, Vs] = X^T [H, N64] . dz^T [Vs, N64]^T
-        const GemmGrid g = gemm_grid(h, vs);
-        StoreTransposedEpilogue epi{dw, h, (int)h, (int)vs};
-        hipLaunchKernelGGL(gemm_nt_kernel<StoreTransposedEpilogue>, dim3(g.blocks()), dim3(kThreads),
-                           0, stream, Operand{xt, b.n_ld, (int)h}, Operand{dzt, b.n_ld, (int)vs},
-                           (int)b.n_ld, g.tiles_m, g.tiles_n, epi);
-    }
-    return hipGetLastError();
+    float *part = (float *)(base + b.off_split);
+    // C^T [H, cols] = A [H, K] . B [cols, K]^T stored as out [cols, H]; split over K (into
+    // the partials, then summed into out) when the output has too few tiles
+    auto gemm = [&](Operand A, Operand B, int64_t K, int64_t cols, int64_t splits, int64_t chunk,
+                    float *out) -> hipError_t {
+        const GemmGrid g = gemm_grid(h, cols);
+        if (splits == 1) {
+            StoreTransposedEpilogue epi{out, h, (int)h, (int)cols};
+            hipLaunchKernelGGL(gemm_nt_kernel<StoreTransposedEpilogue>, dim3(g.blocks()),
+                               dim3(kThreads), 0, stream, A, B, (int)K, g.tiles_m, g.tiles_n, epi);
+            return hipGetLastError();
+        }
+        StoreTransposedEpilogue epi{part, h, (int)h, (int)cols};
+        hipLaunchKernelGGL(gemm_nt_splitk_store_kernel, dim3((unsigned)(g.blocks() * splits)),
+                           dim3(kThreads), 0, stream, A, B, (int)K, (int)chunk, g.tiles_m,
+                           g.tiles_n, epi, cols * h);
+        const int64_t count = cols * h;
+        hipLaunchKernelGGL(sum_splits_kernel,
+                           dim3((unsigned)std::min<int64_t>(ceil_div(count / 4, 256), 8192)),
+                           dim3(256), 0, stream, part, (int)splits, count, count, out);
+        return hipGetLastError();
+    };
+    hipError_t e;
+    // dX_r^T [H, N] = W_r^T [H, Vs64] . dz [N, Vs64]^T
+    if ((e = gemm(Operand{wt, b.vs_ld, (int)h}, Operand{dz, b.vs_ld, (int)n}, b.vs_ld, n,
+                  b.splits_dx, b.chunk_dx, dx)) != hipSuccess)
+        return e;
+    // dW_r^T [H, Vs] = X^T [H, N64] . dz^T [Vs, N64]^T
+    return gemm(Operand{xt, b.n_ld, (int)h}, Operand{dzt, b.n_ld, (int)vs}, b.n_ld, vs, b.splits_dw,
+                b.chunk_dw, dw);
 }
 
 hipError_t launch_bwd_zero_dw(float *dw, int64_t vs, int64_t h, hipStream_t stream) {

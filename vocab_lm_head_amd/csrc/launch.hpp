@@ -23,6 +23,9 @@ FwdWorkspace fwd_workspace(int64_t n, int64_t vs);
 struct BwdWorkspace {
     int64_t n_ld, vs_ld;   // padded leading dimensions (multiples of 64)
     size_t off_xt, off_wt, off_dz, off_dzt;
+    // split-K of the two gradient GEMMs (1: none) and the partials region they share
+    int64_t splits_dx, chunk_dx, splits_dw, chunk_dw;
+    size_t off_split;
     size_t bytes;
 };
 BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs);
