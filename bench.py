@@ -58,16 +58,22 @@ CE_SOURCES = ("common.hpp", "gemm.hpp", "launch.hpp", "ce_fwd.hip", "ce_combine.
 
 
 def kernel_source_hash() -> str:
-    """Hash of everything that decides the CE sequence's kernel code: its sources and the
-    build script (flags).  The counter summaries record it, so that a reading taken on
-    other kernels is never reported."""
+    """Hash of everything that decides the CE sequence's kernel code: its sources, the
+    compile command and the device flags of the build script.  The counter summaries record
+    it, so that a reading taken on other kernels is never reported."""
+    import importlib.util
+    import inspect
+    spec = importlib.util.spec_from_file_location(
+        "vp_build", os.path.join(ROOT, "vocab_lm_head_amd", "build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
     h = hashlib.sha256()
-    files = [os.path.join(ROOT, "vocab_lm_head_amd", "csrc", f) for f in CE_SOURCES]
-    files.append(os.path.join(ROOT, "vocab_lm_head_amd", "build.py"))
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for f in CE_SOURCES:
+        h.update(f.encode())
+        with open(os.path.join(ROOT, "vocab_lm_head_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(inspect.getsource(build._compile).encode())
+    h.update(repr((build.ARCH, build.DEVICE_FLAGS)).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,7 +15,7 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LIB = os.path.join(ROOT, "vocab_lm_head_amd", "libvplmhead.so")
+LIB = os.environ.get("VP_LMHEAD_LIB") or os.path.join(ROOT, "vocab_lm_head_amd", "libvplmhead.so")
 
 OK, NULL, SHAPE, RANGE, ALIGN, WORKSPACE, HIP = 0, -1, -2, -3, -4, -5, -6
 
@@ -227,6 +227,7 @@ def test_bwd_validation_and_workspace(lib):
 def test_product_package_fails_loudly_without_library(tmp_path, monkeypatch):
     """The binding must raise (not fall back) when the shared library is absent."""
     import importlib.util
+    monkeypatch.delenv("VP_LMHEAD_LIB", raising=False)   # no other build of it either
     src = os.path.join(ROOT, "vocab_lm_head_amd", "_lib.py")
     dst = tmp_path / "_lib.py"
     dst.write_text(open(src).read())   # a copy with no libvplmhead.so beside it

@@ -15,7 +15,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvplmhead.so")
+# VP_LMHEAD_LIB selects another build of the same library (e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("VP_LMHEAD_LIB") or os.path.join(_HERE, "libvplmhead.so")
 
 VP_OK = 0
 DEFAULT_IGNORE_INDEX = -100

@@ -1,6 +1,7 @@
 """Build ``libvplmhead.so`` (HIP C++ for gfx950) in-tree with hipcc.
 
-    python vocab_lm_head_amd/build.py          # compile every source, link the library
+    python vocab_lm_head_amd/build.py             # compile every source, link the library
+    python vocab_lm_head_amd/build.py --sanitize  # host side under ASan + UBSan, in _build/
 
 (Run it by path: importing the package loads the library this script builds.)
 
@@ -42,8 +43,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm under /opt/rocm)")
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra: list[str], out_dir: str = BUILD) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
            "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, *extra, "-c",
            os.path.join(CSRC, src), "-o", obj]
@@ -60,22 +61,34 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = True, extra: list[str] | None = None) -> str:
-    """Compile every HIP/C++ source for gfx950 and link ``libvplmhead.so``. Returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra or [])
+# host-side AddressSanitizer + UndefinedBehaviorSanitizer (the device code is unchanged)
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZED_LIB = os.path.join(BUILD, "sanitize", "libvplmhead.so")
+
+
+def build(verbose: bool = True, extra: list[str] | None = None, sanitize: bool = False) -> str:
+    """Compile every HIP/C++ source for gfx950 and link ``libvplmhead.so``. Returns its path.
+
+    ``sanitize``: build the host side under ASan + UBSan into ``_build/sanitize/`` instead
+    (load it with VP_LMHEAD_LIB and the ASan runtime preloaded)."""
+    out_dir = os.path.dirname(SANITIZED_LIB) if sanitize else BUILD
+    lib_path = SANITIZED_LIB if sanitize else LIB
+    os.makedirs(out_dir, exist_ok=True)
+    extra = list(extra or []) + (SANITIZE_HOST if sanitize else [])
     with concurrent.futures.ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, extra, out_dir), SOURCES))
+    tmp = lib_path + ".tmp"
+    link_san = ["-fsanitize=address,undefined", "-shared-libsan"] if sanitize else []
+    cmd = [hipcc(), f"--offload-arch={ARCH}", *link_san, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv[1:])
