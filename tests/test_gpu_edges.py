@@ -79,6 +79,38 @@ def test_ignore_index(vp):
         assert not host(out["grads"][t][0])[ign].any(), "ignored tokens must get dX = 0"
 
 
+def test_ignore_index_inside_the_vocabulary(vp):
+    """ignore_index = 517, a real id of shard 1 (V = 1024, T = 2): every 7th token targets it
+    and is ignored -- loss 0, no gradient, left out of the mean -- although each shard's
+    forward still picks its logit as that token's target (the statistics do not know which
+    id is ignored)."""
+    xb, wb, y = _problem(9, 300, 64, 1024)
+    ign = 517
+    y[::7] = ign
+    N, H = xb.shape
+    V, T = wb.shape[0], 2
+    x, w = vp_inputs.bf16_bits_to_f64(xb), vp_inputs.bf16_bits_to_f64(wb)
+    z = oracle.logits(x, w)
+    loss, lse, mean = oracle.dense_ce(z, y, ignore_index=ign)
+    dz = oracle.dense_dlogits(z, y, ignore_index=ign)
+    g = oracle.mean_scale(y, ign)
+    rng = [oracle.shard_range(V, T, t) for t in range(T)]
+    x_d, w_d, y_d = dev_bf16(xb), dev_bf16(wb), dev_i64(y)
+    out = run_ce_path(vp, x_d, [w_d[a:b] for a, b in rng], [a for a, _ in rng],
+                      [b for _, b in rng], y_d, g, bwd_shards=[0, 1], ignore_index=ign)
+    for t, (a, b) in enumerate(rng):
+        assert_stats_close((host(out["m"][t]), host(out["s"][t]), host(out["zy"][t])),
+                           oracle.shard_stats(z[:, a:b], y, a), f"shard {t} stats")
+    assert_loss_close(host(out["loss"]), loss)
+    assert not host(out["loss"])[y == ign].any()
+    assert abs(float(out["mean"].item()) - mean) <= 2e-3
+    for t, (a, b) in enumerate(rng):
+        dxr, dwr = oracle.shard_grads(x, w[a:b], dz[:, a:b])
+        assert_grad_close(host(out["grads"][t][0]), dxr, f"dX partial {t}")
+        assert_grad_close(host(out["grads"][t][1]), dwr, f"dW {t}")
+        assert not host(out["grads"][t][0])[y == ign].any(), "ignored tokens must get dX = 0"
+
+
 def test_all_ignored(vp):
     """N_valid = 0: mean 0 (max(1, N_valid) guard), loss 0, every gradient 0."""
     xb, wb, y = _problem(3, 40, 32, 96)
