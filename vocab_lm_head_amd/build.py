@@ -1,6 +1,7 @@
 """Build ``libvplmhead.so`` (HIP C++ for gfx950) in-tree with hipcc.
 
     python vocab_lm_head_amd/build.py             # compile every source, link the library
+                                                  # (and the C-ABI test program)
     python vocab_lm_head_amd/build.py --sanitize  # host side under ASan + UBSan, in _build/
 
 (Run it by path: importing the package loads the library this script builds.)
@@ -90,5 +91,25 @@ def build(verbose: bool = True, extra: list[str] | None = None, sanitize: bool =
     return lib_path
 
 
+C_DRIVER_SRC = os.path.join(ROOT, "tests", "c_abi", "vp_step.cpp")
+C_DRIVER = os.path.join(ROOT, "tests", "c_abi", "vp_step")
+
+
+def build_c_driver(verbose: bool = True) -> str:
+    """Compile the C-ABI test program (host code linked against libvplmhead.so, found next
+    to this file at run time)."""
+    cmd = [hipcc(), "-O2", "-std=c++17", "-Wall", "-I", INCLUDE, C_DRIVER_SRC, "-L", PKG,
+           "-lvplmhead", "-Wl,-rpath,$ORIGIN/../../vocab_lm_head_amd", "-o", C_DRIVER]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the C-ABI test program:\n{' '.join(cmd)}\n{r.stderr}")
+    if verbose:
+        print(f"built {C_DRIVER}")
+    return C_DRIVER
+
+
 if __name__ == "__main__":
-    build(sanitize="--sanitize" in sys.argv[1:])
+    sanitize = "--sanitize" in sys.argv[1:]
+    build(sanitize=sanitize)
+    if not sanitize:
+        build_c_driver()
