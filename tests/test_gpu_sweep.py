@@ -1,0 +1,77 @@
+"""A seeded sweep of 24 random small shapes through the whole CE path, each compared in full
+with the oracle: odd N, H (a multiple of 8) and Vs, T = 1..5, 10% ignored targets.  The
+shapes are drawn so that the forward's slice merge runs in one pass and split 2-5 ways,
+and the gradient GEMMs run single-pass and split over K 2-16 ways, in many combinations.
+Same bars as the other parity tests."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import vp_inputs
+from gpu_util import (assert_grad_close, assert_loss_close, assert_stats_close, dev_bf16, dev_i64,
+                      host, log, run_ce_path)
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases():
+    r = np.random.default_rng(2024)
+    out = []
+    for i in range(24):
+        T = int(r.integers(1, 6))
+        if i % 4 == 0:     # few tokens, a wide shard: the merge splits, dX splits over K
+            N, H, Vs = int(r.integers(1, 200)), 8 * int(r.integers(1, 17)), int(r.integers(8000, 24000))
+            T = min(T, 2)
+        elif i % 4 == 1:   # many tokens, a narrow shard: dW splits over K
+            N, H, Vs = int(r.integers(1000, 3000)), 8 * int(r.integers(1, 65)), int(r.integers(1, 1500))
+        elif i % 4 == 2:
+            N, H, Vs = int(r.integers(1, 700)), 8 * int(r.integers(1, 129)), int(r.integers(1, 3000))
+        else:
+            N, H, Vs = int(r.integers(300, 1500)), 8 * int(r.integers(8, 65)), int(r.integers(1000, 4000))
+        out.append((i, N, H, Vs, T))
+    return out
+
+
+@pytest.fixture(scope="module")
+def vp():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vocab_lm_head_amd
+    return vocab_lm_head_amd
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"{c[0]}-N{c[1]}-H{c[2]}-Vs{c[3]}-T{c[4]}")
+def test_random_shape(vp, case):
+    i, N, H, Vs, T = case
+    V = Vs * T
+    r = np.random.default_rng(1000 + i)
+    xb = vp_inputs.f32_to_bf16_bits(r.standard_normal((N, H)).astype(np.float32))
+    wb = vp_inputs.f32_to_bf16_bits(
+        r.standard_normal((V, H)).astype(np.float32) * np.float32(3.0 / math.sqrt(H)))
+    y = r.integers(0, V, N).astype(np.int64)
+    y[r.random(N) < 0.1] = oracle.DEFAULT_IGNORE_INDEX
+    log(f"  case {i}: N={N} H={H} Vs={Vs} T={T}")
+    x, w = vp_inputs.bf16_bits_to_f64(xb), vp_inputs.bf16_bits_to_f64(wb)
+    z = oracle.logits(x, w)
+    loss, lse, mean = oracle.dense_ce(z, y)
+    dz = oracle.dense_dlogits(z, y)
+    g = oracle.mean_scale(y)
+    rng = [oracle.shard_range(V, T, t) for t in range(T)]
+    x_d, w_d, y_d = dev_bf16(xb), dev_bf16(wb), dev_i64(y)
+    out = run_ce_path(vp, x_d, [w_d[a:b] for a, b in rng], [a for a, _ in rng],
+                      [b for _, b in rng], y_d, g, bwd_shards=range(T))
+    for t, (a, b) in enumerate(rng):
+        assert_stats_close((host(out["m"][t]), host(out["s"][t]), host(out["zy"][t])),
+                           oracle.shard_stats(z[:, a:b], y, a), f"shard {t} stats")
+    assert_loss_close(host(out["loss"]), loss)
+    assert_loss_close(host(out["lse"]), lse, "lse")
+    assert abs(float(out["mean"].item()) - mean) <= 2e-3
+    for t, (a, b) in enumerate(rng):
+        dxr, dwr = oracle.shard_grads(x, w[a:b], dz[:, a:b])
+        assert_grad_close(host(out["grads"][t][0]), dxr, f"dX partial {t}")
+        assert_grad_close(host(out["grads"][t][1]), dwr, f"dW {t}")
