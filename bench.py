@@ -57,10 +57,14 @@ def log(msg):
 CE_SOURCES = ("common.hpp", "gemm.hpp", "launch.hpp", "ce_fwd.hip", "ce_combine.hip", "ce_bwd.hip")
 
 
-def kernel_source_hash() -> str:
-    """Hash of everything that decides the CE sequence's kernel code: its sources, the
-    compile command and the device flags of the build script.  The counter summaries record
-    it, so that a reading taken on other kernels is never reported."""
+# the sources the lookup's and its gradient's kernels are compiled from
+LOOKUP_SOURCES = ("common.hpp", "launch.hpp", "embed.hip", "embed_bwd.hip")
+
+
+def kernel_source_hash(sources=CE_SOURCES) -> str:
+    """Hash of everything that decides the kernels' code: their sources (the CE sequence's
+    by default), the compile command and the device flags of the build script.  The counter
+    summaries record it, so that a reading taken on other kernels is never reported."""
     import importlib.util
     import inspect
     spec = importlib.util.spec_from_file_location(
@@ -68,7 +72,7 @@ def kernel_source_hash() -> str:
     build = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(build)
     h = hashlib.sha256()
-    for f in CE_SOURCES:
+    for f in sources:
         h.update(f.encode())
         with open(os.path.join(ROOT, "vocab_lm_head_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
@@ -104,6 +108,81 @@ def short_kernel_name(name: str) -> str:
         return m.group(1)
     m = re.search(r"(\w+)(?:<[^<>()]*>)?\(", name)
     return m.group(1) if m else name
+
+
+LOOKUP_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_lookup_embedding_heavy.txt")
+EMBED_HEAVY_GRID = "4194304"   # the embedding-heavy lookup's launch: 65536 rows, 4 per workgroup
+LOOKUP_GRAD_KERNELS = ("radix_count_kernel", "radix_scan_kernel", "radix_scatter_kernel",
+                       "radix_count_kernel", "radix_scan_kernel", "radix_scatter_kernel",
+                       "segment_sum_kernel", "segment_fixup_kernel")
+
+
+def recorded_lookup_traffic():
+    """HBM bytes of one embedding-heavy lookup and of one call of its weight gradient, from
+    the committed counter summary, if the kernels are still the ones it was measured on."""
+    try:
+        txt = open(LOOKUP_TRAFFIC_PROFILE).read()
+    except OSError:
+        return {}
+    h = re.search(r"^kernel_source_hash: (\w+)", txt, re.M)
+    if not h or h.group(1) != kernel_source_hash(LOOKUP_SOURCES):
+        return {}
+    out = {}
+    for key in ("lookup", "gradient"):
+        b = re.search(rf"^{key}_traffic_bytes: (\d+)", txt, re.M)
+        if b:
+            out[key] = int(b.group(1))
+    return out
+
+
+def _pmc_rows_grid(path, counter):
+    """[(dispatch id, short kernel name, grid size, value)] of one counter."""
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = int(r["Dispatch_Id"])
+        acc.setdefault(k, [short_kernel_name(r["Kernel_Name"]), r.get("Grid_Size", ""), 0.0])[2] += \
+            float(r["Counter_Value"])
+    return sorted((k, v[0], v[1], v[2]) for k, v in acc.items())
+
+
+def reduce_pmc_lookup(fetch_csv, write_csv, cmd_fetch, cmd_write):
+    """Summarise two counter runs of this script (FETCH_SIZE, WRITE_SIZE) into
+    LOOKUP_TRAFFIC_PROFILE: the last embedding-heavy lookup launch and the last call of its
+    weight gradient (its eight kernels), each counter scaled by its reading for the 1 GiB
+    device copy of the yardsticks."""
+    sel = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows_grid(path, name)
+        copies = [v for _, k, _, v in rows if "copyBuffer" in k and v > 0.5 * COPY_BYTES / 1024]
+        factor = (COPY_BYTES / 1024) / (sum(copies) / len(copies))
+        i_look = max(i for i, (_, k, g, _) in enumerate(rows)
+                     if k == "embed_kernel" and g == EMBED_HEAVY_GRID)
+        i_fix = max(i for i, (_, k, _, _) in enumerate(rows) if k == "segment_fixup_kernel")
+        grad = rows[i_fix - len(LOOKUP_GRAD_KERNELS) + 1:i_fix + 1]
+        assert tuple(k for _, k, _, _ in grad) == LOOKUP_GRAD_KERNELS, "unexpected kernel sequence"
+        sel[name] = (factor, rows[i_look][3], [(k, v) for _, k, _, v in grad], len(copies))
+    f_f, look_f, grad_f, nf = sel["FETCH_SIZE"]
+    f_w, look_w, grad_w, nw = sel["WRITE_SIZE"]
+    look = (look_f * f_f + look_w * f_w) * 1024
+    grad = (sum(v for _, v in grad_f) * f_f + sum(v for _, v in grad_w) * f_w) * 1024
+    lines = ["# HBM traffic of the embedding-heavy lookup (65536 Zipf(1.0) ids on shard 0 = [64000, 4096]",
+             "# of V=256000) and of one call of its weight gradient, from rocprofv3 counters.",
+             "# commands (from the repository root):", f"#   {cmd_fetch}", f"#   {cmd_write}",
+             "#   python3 bench.py --reduce-pmc-lookup <fetch csv> <write csv>   (writes this file)",
+             "# Each counter is scaled by its reading for the 1 GiB device copy of the yardsticks.",
+             f"kernel_source_hash: {kernel_source_hash(LOOKUP_SOURCES)}",
+             f"copy_calibration: FETCH factor {f_f:.4f} ({nf} copies), WRITE factor {f_w:.4f} ({nw} copies)",
+             "", "kernel                      FETCH_KiB    WRITE_KiB   (raw counter)",
+             f"{'embed_kernel':26s} {look_f:12.0f} {look_w:12.0f}"]
+    for (k, vf), (_, vw) in zip(grad_f, grad_w):
+        lines.append(f"{k:26s} {vf:12.0f} {vw:12.0f}")
+    lines += ["", f"lookup_traffic_bytes: {int(round(look))}",
+              f"gradient_traffic_bytes: {int(round(grad))}"]
+    with open(LOOKUP_TRAFFIC_PROFILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def _pmc_rows(path, counter):
@@ -255,6 +334,9 @@ def main():
     ap.add_argument("--reduce-mfma", metavar="COUNTER_CSV",
                     help="summarise a rocprofv3 --pmc run of this script with MFMA_COUNTERS and "
                          "--kernel-trace into profiles/ and exit (no GPU needed)")
+    ap.add_argument("--reduce-pmc-lookup", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script's lookup benches into profiles/ and exit (no GPU needed)")
     ap.add_argument("--reduce-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script into profiles/ and exit (no GPU needed)")
@@ -272,6 +354,13 @@ def main():
         cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {os.path.dirname(path)} {run_args}"
                 for c, path in zip(("FETCH_SIZE", "WRITE_SIZE"), args.reduce_pmc)]
         reduce_pmc(args.reduce_pmc[0], args.reduce_pmc[1], cmds[0], cmds[1])
+        return
+    if args.reduce_pmc_lookup:
+        look_args = "-o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline " \
+                    "--no-comparator --no-other-workloads"
+        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {os.path.dirname(path)} {look_args}"
+                for c, path in zip(("FETCH_SIZE", "WRITE_SIZE"), args.reduce_pmc_lookup)]
+        reduce_pmc_lookup(args.reduce_pmc_lookup[0], args.reduce_pmc_lookup[1], cmds[0], cmds[1])
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (each vocab "
@@ -597,7 +686,8 @@ def embed_bench(torch, vp, vp_inputs, dev, stream, args):
     ms = float(np.median(times))
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": gbs / PEAK_HBM_GBS, "median_ms": ms, "min_ms": float(np.min(times)),
+            "frac": gbs / PEAK_HBM_GBS, "traffic": recorded_lookup_traffic().get("lookup"),
+            "median_ms": ms, "min_ms": float(np.min(times)),
             "algorithmic_bytes": alg_bytes, "distinct_on_shard_rows": distinct,
             "on_shard_ids": int(own.size), "bit_exact_sample": ok}
 
@@ -749,7 +839,8 @@ def embed_bwd_bench(torch, vp, vp_inputs, dev, stream, args, keep=None):
     ms = float(np.median(times))
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": gbs / PEAK_HBM_GBS, "median_ms": ms, "min_ms": float(np.min(times)),
+            "frac": gbs / PEAK_HBM_GBS, "traffic": recorded_lookup_traffic().get("gradient"),
+            "median_ms": ms, "min_ms": float(np.min(times)),
             "algorithmic_bytes": alg_bytes, "owned_ids": int(own.sum()),
             "distinct_rows": int(rows.size), "most_repeated_row": int(counts.max()),
             "sample_max_rel_err": sample_err, "deterministic": deterministic}
