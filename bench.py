@@ -63,8 +63,9 @@ LOOKUP_SOURCES = ("common.hpp", "launch.hpp", "embed.hip", "embed_bwd.hip")
 
 def kernel_source_hash(sources=CE_SOURCES) -> str:
     """Hash of everything that decides the kernels' code: their sources (the CE sequence's
-    by default), the compile command and the device flags of the build script.  The counter
-    summaries record it, so that a reading taken on other kernels is never reported."""
+    by default, comments and layout stripped), the compile command and the device flags of
+    the build script.  The counter summaries record it, so that a reading taken on other
+    kernels is never reported."""
     import importlib.util
     import inspect
     spec = importlib.util.spec_from_file_location(
@@ -74,8 +75,11 @@ def kernel_source_hash(sources=CE_SOURCES) -> str:
     h = hashlib.sha256()
     for f in sources:
         h.update(f.encode())
-        with open(os.path.join(ROOT, "vocab_lm_head_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "vocab_lm_head_amd", "csrc", f)) as fh:
+            src = fh.read()
+        # comments and layout do not change the code: only the tokens are hashed
+        src = re.sub(r"/\*.*?\*/|//[^\n]*", " ", src, flags=re.S)
+        h.update(" ".join(src.split()).encode())
     h.update(inspect.getsource(build._compile).encode())
     h.update(repr((build.ARCH, build.DEVICE_FLAGS)).encode())
     return h.hexdigest()[:16]

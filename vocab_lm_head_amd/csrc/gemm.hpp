@@ -16,10 +16,11 @@
 // LDS rows are 64 bf16 = 128 B = eight 16-byte chunks; chunk c of row r is
 // stored at chunk c ^ (r & 7) so that the 16-lane groups of a fragment read
 // (16 consecutive rows, one chunk) hit distinct banks.
-// Global -> LDS goes through buffer loads straight into LDS (buffer_load ... lds),
-// two K steps ahead; operand fragments are double-buffered in registers so
-// that the LDS reads of one half K step overlap the MFMAs of the other; one
-// barrier per K step.
+// Global -> LDS goes through buffer loads straight into LDS (buffer_load ... lds):
+// the loads of K step k+2 are issued in the second half of step k, into the stage
+// step k has just finished with.  Operand fragments are double-buffered in
+// registers so that the LDS reads of one half K step overlap the MFMAs of the
+// other; one barrier per K step.
 //
 // Rows past M / N read as zeros (outside the buffer resource; the epilogue
 // masks them); K chunks past K are zero-filled, so K need only be a multiple
