@@ -641,9 +641,30 @@ def ce_workload_bench(torch, vp, vp_inputs, dev, stream, args, name):
         step(marks[k])
     torch.cuda.synchronize()
     t = np.array([mk[0].elapsed_time(mk[1]) for mk in marks])
+    # the same step captured once in a HIP graph and replayed (no per-kernel launch cost)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    gt = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        gt.append(a.elapsed_time(b))
     ms = float(np.median(t))
     tf = 6.0 * N * Vs * H / (ms * 1e-3) / 1e12
     out.update({"median_ms": ms, "min_ms": float(t.min()), "steps": steps,
+                "graph_replay_median_ms": float(np.median(gt)),
                 "tokens_per_s": N / (ms * 1e-3), "achieved_tflops": tf,
                 "frac": tf / PEAK_BF16_TFLOPS, "executed_tflops": tf * 8.0 / 6.0})
     return out
