@@ -111,6 +111,39 @@ def test_ignore_index_inside_the_vocabulary(vp):
         assert not host(out["grads"][t][0])[y == ign].any(), "ignored tokens must get dX = 0"
 
 
+def test_out_of_range_targets_follow_the_contract(vp):
+    """Targets outside [0, V) that are not ignore_index (V + 5, -7, 2^40) break the data
+    contract; the header defines what the GPU then does: such a target is off-shard on every
+    shard, so no shard picks a target logit (loss = lse), the token still counts in the mean,
+    and its gradient has no onehot term.  Expected values: the oracle on the same tokens with
+    those targets replaced by 0, then the onehot that replacement subtracted added back."""
+    xb, wb, y = _problem(11, 64, 64, 600)
+    bad = np.array([0, 1, 2])
+    y[bad] = [600 + 5, -7, 2**40]
+    N, V, T = 64, 600, 3
+    x, w = vp_inputs.bf16_bits_to_f64(xb), vp_inputs.bf16_bits_to_f64(wb)
+    z = oracle.logits(x, w)
+    y_rep = y.copy()
+    y_rep[bad] = 0
+    loss, lse, _ = oracle.dense_ce(z, y_rep)
+    loss[bad] = lse[bad]
+    mean = loss.sum() / N
+    g = oracle.mean_scale(y)                        # all 64 tokens count
+    dz = oracle.dense_dlogits(z, y_rep, scale=g)
+    dz[bad, 0] += g
+    rng = [oracle.shard_range(V, T, t) for t in range(T)]
+    x_d, w_d, y_d = dev_bf16(xb), dev_bf16(wb), dev_i64(y)
+    out = run_ce_path(vp, x_d, [w_d[a:b] for a, b in rng], [a for a, _ in rng],
+                      [b for _, b in rng], y_d, g, bwd_shards=range(T))
+    assert_loss_close(host(out["loss"]), loss)
+    assert_loss_close(host(out["lse"]), lse, "lse")
+    assert abs(float(out["mean"].item()) - mean) <= 2e-3
+    for t, (a, b) in enumerate(rng):
+        dxr, dwr = oracle.shard_grads(x, w[a:b], dz[:, a:b])
+        assert_grad_close(host(out["grads"][t][0]), dxr, f"dX partial {t}")
+        assert_grad_close(host(out["grads"][t][1]), dwr, f"dW {t}")
+
+
 def test_all_ignored(vp):
     """N_valid = 0: mean 0 (max(1, N_valid) guard), loss 0, every gradient 0."""
     xb, wb, y = _problem(3, 40, 32, 96)
