@@ -247,6 +247,30 @@ def test_deterministic(vp):
             assert torch.equal(runs[0]["grads"][t][k], runs[1]["grads"][t][k]), (t, k)
 
 
+@pytest.mark.parametrize("scale", [1.0, 0.0, -0.25, 4096.0])
+def test_grad_scale_other_than_the_mean(vp, scale):
+    """grad_scale is the caller's upstream factor: 1 for a summed loss, 0, a negative one,
+    and a loss-scaling factor.  dX and dW follow the oracle's dlogits at that factor, and
+    at 0 both are exactly zero."""
+    xb, wb, y = _problem(91, 300, 136, 1400, ignore_frac=0.1)
+    x, w = vp_inputs.bf16_bits_to_f64(xb), vp_inputs.bf16_bits_to_f64(wb)
+    z = oracle.logits(x, w)
+    dz = oracle.dense_dlogits(z, y, scale=scale)
+    rng = [oracle.shard_range(1400, 2, t) for t in range(2)]
+    x_d, w_d, y_d = dev_bf16(xb), dev_bf16(wb), dev_i64(y)
+    log(f"  grad_scale {scale}")
+    out = run_ce_path(vp, x_d, [w_d[a:b] for a, b in rng], [a for a, _ in rng],
+                      [b for _, b in rng], y_d, scale, bwd_shards=[0, 1])
+    for t, (a, b) in enumerate(rng):
+        dxr, dwr = oracle.shard_grads(x, w[a:b], dz[:, a:b])
+        dx, dw = host(out["grads"][t][0]), host(out["grads"][t][1])
+        if scale == 0.0:
+            assert not dx.any() and not dw.any(), "grad_scale 0 must give zero gradients"
+        else:
+            assert_grad_close(dx, dxr, f"dX partial {t}")
+            assert_grad_close(dw, dwr, f"dW {t}")
+
+
 def test_large_logits(vp):
     """Logit std 40: the stabilising maximum matters; sum-exp must not overflow."""
     xb, wb, y = _problem(7, 130, 128, 640, logit_std=40.0)
