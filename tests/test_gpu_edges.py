@@ -371,3 +371,41 @@ def test_invalid_arguments_raise(vp):
     assert e.value.status == -4
     with pytest.raises(vp.VPError):
         vp.vp_shard_range(10, 4, 0)
+
+
+def test_binding_rejects_mismatched_buffers(vp):
+    """The binding refuses caller buffers the kernels would overrun or could not address,
+    before anything is launched: short outputs, a host workspace, an undersized one."""
+    import torch
+    d = "cuda"
+    n, h, vs = 64, 16, 40
+    x = torch.zeros((n, h), dtype=torch.bfloat16, device=d)
+    w = torch.zeros((vs, h), dtype=torch.bfloat16, device=d)
+    y = torch.zeros(n, dtype=torch.int64, device=d)
+    lse = torch.zeros(n, dtype=torch.float32, device=d)
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32, device=d)
+    with pytest.raises(ValueError):
+        vp.vp_lmhead_ce_bwd(x, w, y, lse, 0, vs, 1.0, dx=f32(n - 1, h))
+    with pytest.raises(ValueError):
+        vp.vp_lmhead_ce_bwd(x, w, y, lse, 0, vs, 1.0, dw=f32(vs, h - 8))
+    with pytest.raises(ValueError):
+        vp.vp_lmhead_ce_bwd(x, w, y, lse, 0, vs, 1.0,
+                            workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(vp.VPError) as e:
+        vp.vp_lmhead_ce_bwd(x, w, y, lse, 0, vs, 1.0,
+                            workspace=torch.zeros(64, dtype=torch.uint8, device=d))
+    assert e.value.status == -5
+    with pytest.raises(ValueError):
+        vp.vp_lmhead_ce_fwd(x, w, y, 0, vs, m_local=f32(n // 2))
+    logits = vp.vp_lmhead_logits(x, w, 0, vs)
+    with pytest.raises(ValueError):
+        vp.vp_logits_ce_stats(logits, y, 0, vs, s_local=f32(n + 1))
+    with pytest.raises(ValueError):
+        vp.vp_logits_ce_bwd(logits, x, w, y, lse, 0, vs, 1.0, dx=f32(n, h + 8))
+    with pytest.raises(ValueError):
+        vp.vp_logits_ce_bwd(logits, x, w, y[: n - 1], lse, 0, vs, 1.0)
+    with pytest.raises(ValueError):
+        vp.vp_ce_max(f32(2, n), out=f32(n - 1))
+    with pytest.raises(ValueError):
+        vp.vp_embed_bwd(y, x, 0, vs, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+    torch.cuda.synchronize()

@@ -78,13 +78,35 @@ def _check(status: int, where: str) -> None:
         raise VPError(status, where)
 
 
-def _stream(stream=None) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
+def _stream(stream, device) -> int:
+    """The given stream, else the current stream of the tensors' device."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream
+
+
+def _same_device(*tensors):
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one GPU, got {sorted(map(str, devs))}")
+
+
+def _workspace(workspace, need, device):
+    """The caller's workspace (the library checks its size), else a new one."""
+    if workspace is None:
+        return alloc_workspace(need, device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace
 
 
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
+
+
+def _shape(t, shape, name):
+    """Caller-provided buffers must have exactly the shape the kernels write or read."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
 
 
 def _need(t, dtype, ndim, name):
@@ -127,8 +149,9 @@ def vp_embed_fwd(ids, w_shard, vocab_start: int, vocab_end: int, out=None, strea
     _need(out, torch.bfloat16, 2, "out")
     if tuple(out.shape) != (n, h):
         raise ValueError("out must be [n, h]")
+    _same_device(ids, w_shard, out)
     _check(lib.vp_embed_fwd(_ptr(ids), n, _ptr(w_shard), int(vocab_start), int(vocab_end), h,
-                            _ptr(out), _stream(stream)), "vp_embed_fwd")
+                            _ptr(out), _stream(stream, out.device)), "vp_embed_fwd")
     return out
 
 
@@ -151,11 +174,11 @@ def vp_embed_bwd(ids, dout, vocab_start: int, vocab_end: int, dw=None, workspace
     if tuple(dw.shape) != (vs, h):
         raise ValueError("dw must be [vocab_end - vocab_start, h]")
     need = vp_embed_bwd_workspace(n, h, vocab_start, vocab_end)
-    if workspace is None:
-        workspace = alloc_workspace(need, dout.device)
+    workspace = _workspace(workspace, need, dout.device)
+    _same_device(ids, dout, dw, workspace)
     _check(lib.vp_embed_bwd(_ptr(ids), n, _ptr(dout), int(vocab_start), int(vocab_end), h,
                             _ptr(dw), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                            _stream(stream)), "vp_embed_bwd")
+                            _stream(stream, dw.device)), "vp_embed_bwd")
     return dw
 
 
@@ -191,12 +214,12 @@ def vp_lmhead_ce_fwd(hidden, w_shard, targets, vocab_start: int, vocab_end: int,
             raise ValueError("statistics outputs must have n elements")
         outs.append(t)
     need = vp_lmhead_ce_fwd_workspace(n, h, vocab_start, vocab_end)
-    if workspace is None:
-        workspace = alloc_workspace(need, dev)
+    workspace = _workspace(workspace, need, dev)
+    _same_device(hidden, w_shard, targets, *outs, workspace)
     _check(lib.vp_lmhead_ce_fwd(_ptr(hidden), _ptr(w_shard), _ptr(targets), n, h, int(vocab_start),
                                 int(vocab_end), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                _stream(stream)), "vp_lmhead_ce_fwd")
+                                _stream(stream, dev)), "vp_lmhead_ce_fwd")
     return tuple(outs)
 
 
@@ -217,8 +240,9 @@ def vp_ce_combine(m, s, zy, targets, ignore_index: int = DEFAULT_IGNORE_INDEX,
         _need(t, torch.float32, 1, nm)
         if t.shape[0] != size:
             raise ValueError(f"{nm} must have {size} elements")
+    _same_device(m, s, zy, targets, loss, lse, loss_mean)
     _check(lib.vp_ce_combine(_ptr(m), _ptr(s), _ptr(zy), _ptr(targets), n, T, int(ignore_index),
-                             _ptr(loss), _ptr(lse), _ptr(loss_mean), _stream(stream)),
+                             _ptr(loss), _ptr(lse), _ptr(loss_mean), _stream(stream, dev)),
            "vp_ce_combine")
     return loss, lse, loss_mean
 
@@ -240,13 +264,15 @@ def vp_lmhead_ce_bwd(hidden, w_shard, targets, lse, vocab_start: int, vocab_end:
     dw = torch.empty((vs, h), dtype=torch.float32, device=dev) if dw is None else dw
     _need(dx, torch.float32, 2, "dx")
     _need(dw, torch.float32, 2, "dw")
+    _shape(dx, (n, h), "dx")
+    _shape(dw, (vs, h), "dw")
     need = vp_lmhead_ce_bwd_workspace(n, h, vocab_start, vocab_end)
-    if workspace is None:
-        workspace = alloc_workspace(need, dev)
+    workspace = _workspace(workspace, need, dev)
+    _same_device(hidden, w_shard, targets, lse, dx, dw, workspace)
     _check(lib.vp_lmhead_ce_bwd(_ptr(hidden), _ptr(w_shard), _ptr(targets), _ptr(lse), n, h,
                                 int(vocab_start), int(vocab_end), int(ignore_index),
                                 float(grad_scale), _ptr(dx), _ptr(dw), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(stream)),
+                                workspace.numel() * workspace.element_size(), _stream(stream, dev)),
            "vp_lmhead_ce_bwd")
     return dx, dw
 
@@ -271,8 +297,10 @@ def vp_lmhead_logits(hidden, w_shard, vocab_start: int, vocab_end: int, logits=N
     _need(logits, torch.float32, 2, "logits")
     if logits.shape[0] != n:
         raise ValueError("logits must have n rows")
+    _same_device(hidden, w_shard, logits)
     _check(lib.vp_lmhead_logits(_ptr(hidden), _ptr(w_shard), n, h, int(vocab_start), int(vocab_end),
-                                _ptr(logits), logits.shape[1], _stream(stream)), "vp_lmhead_logits")
+                                _ptr(logits), logits.shape[1], _stream(stream, logits.device)),
+           "vp_lmhead_logits")
     return logits
 
 
@@ -283,17 +311,21 @@ def vp_logits_ce_stats(logits, targets, vocab_start: int, vocab_end: int, m_ref=
     _need(logits, torch.float32, 2, "logits")
     _need(targets, torch.int64, 1, "targets")
     n = logits.shape[0]
+    _shape(targets, (n,), "targets")
     dev = logits.device
     outs = []
     for t in (m_local, s_local, zy_local):
         t = torch.empty(n, dtype=torch.float32, device=dev) if t is None else t
         _need(t, torch.float32, 1, "statistics output")
+        _shape(t, (n,), "statistics output")
         outs.append(t)
     if m_ref is not None:
         _need(m_ref, torch.float32, 1, "m_ref")
+        _shape(m_ref, (n,), "m_ref")
+    _same_device(logits, targets, m_ref, *outs)
     _check(lib.vp_logits_ce_stats(_ptr(logits), logits.shape[1], _ptr(targets), n, int(vocab_start),
                                   int(vocab_end), _ptr(m_ref), _ptr(outs[0]), _ptr(outs[1]),
-                                  _ptr(outs[2]), _stream(stream)), "vp_logits_ce_stats")
+                                  _ptr(outs[2]), _stream(stream, dev)), "vp_logits_ce_stats")
     return tuple(outs)
 
 
@@ -303,7 +335,9 @@ def vp_ce_max(m, out=None, stream=None):
     T, n = m.shape
     out = torch.empty(n, dtype=torch.float32, device=m.device) if out is None else out
     _need(out, torch.float32, 1, "out")
-    _check(lib.vp_ce_max(_ptr(m), n, T, _ptr(out), _stream(stream)), "vp_ce_max")
+    _shape(out, (n,), "out")
+    _same_device(m, out)
+    _check(lib.vp_ce_max(_ptr(m), n, T, _ptr(out), _stream(stream, m.device)), "vp_ce_max")
     return out
 
 
@@ -314,17 +348,28 @@ def vp_logits_ce_bwd(logits, hidden, w_shard, targets, lse, vocab_start: int, vo
     _need(logits, torch.float32, 2, "logits")
     _need(hidden, torch.bfloat16, 2, "hidden")
     _need(w_shard, torch.bfloat16, 2, "w_shard")
+    _need(targets, torch.int64, 1, "targets")
+    _need(lse, torch.float32, 1, "lse")
     n, h = hidden.shape
     vs = vocab_end - vocab_start
+    _shape(w_shard, (vs, h), "w_shard")
+    _shape(targets, (n,), "targets")
+    _shape(lse, (n,), "lse")
+    if logits.shape[0] != n:
+        raise ValueError("logits must have n rows")
     dev = hidden.device
     dx = torch.empty((n, h), dtype=torch.float32, device=dev) if dx is None else dx
     dw = torch.empty((vs, h), dtype=torch.float32, device=dev) if dw is None else dw
+    _need(dx, torch.float32, 2, "dx")
+    _need(dw, torch.float32, 2, "dw")
+    _shape(dx, (n, h), "dx")
+    _shape(dw, (vs, h), "dw")
     need = vp_lmhead_ce_bwd_workspace(n, h, vocab_start, vocab_end)
-    if workspace is None:
-        workspace = alloc_workspace(need, dev)
+    workspace = _workspace(workspace, need, dev)
+    _same_device(logits, hidden, w_shard, targets, lse, dx, dw, workspace)
     _check(lib.vp_logits_ce_bwd(_ptr(logits), logits.shape[1], _ptr(hidden), _ptr(w_shard),
                                 _ptr(targets), _ptr(lse), n, h, int(vocab_start), int(vocab_end),
                                 int(ignore_index), float(grad_scale), _ptr(dx), _ptr(dw),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                _stream(stream)), "vp_logits_ce_bwd")
+                                _stream(stream, dev)), "vp_logits_ce_bwd")
     return dx, dw
