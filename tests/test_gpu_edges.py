@@ -195,6 +195,33 @@ def test_combine_many_shards(vp, T):
     assert abs(float(dmean.item()) - mean) <= 2e-3
 
 
+def test_combine_extreme_spreads(vp):
+    """Shard maxima up to 200 apart, so the far shards' rescaled sums underflow to nothing,
+    sums from 1 to Vs, and targets owned by shards far below the global maximum (losses
+    near 200); 10% ignored.  The merge against the oracle's combine in fp64 of the same
+    fp32 statistics."""
+    import torch
+    r = np.random.default_rng(55)
+    T, N, Vs = 8, 2000, 20000
+    m = r.uniform(-100.0, 100.0, (T, N))
+    s = np.exp(r.uniform(0.0, np.log(Vs), (T, N)))
+    owner = r.integers(0, T, N)
+    y = (owner * Vs + r.integers(0, Vs, N)).astype(np.int64)
+    y[r.random(N) < 0.1] = -100
+    zy = np.zeros((T, N))
+    zy[owner, np.arange(N)] = m[owner, np.arange(N)] - r.uniform(0.0, 40.0, N)
+    m, s, zy = (a.astype(np.float32) for a in (m, s, zy))
+    loss, lse, mean = oracle.combine_triples(m.astype(np.float64), s.astype(np.float64),
+                                             zy.astype(np.float64), y)
+    log(f"  losses up to {loss.max():.1f}")
+    dl, dlse, dmean = vp.vp_ce_combine(torch.from_numpy(m).cuda(), torch.from_numpy(s).cuda(),
+                                       torch.from_numpy(zy).cuda(), dev_i64(y))
+    torch.cuda.synchronize()
+    assert_loss_close(host(dl), loss)
+    assert_loss_close(host(dlse), lse, "lse")
+    assert abs(float(dmean.item()) - mean) <= 2e-3
+
+
 def test_twelve_shards_full_path(vp):
     """T=12 (V=1200, Vs=100): every shard's forward, combine over 12, backward of three shards."""
     xb, wb, y = _problem(12, 333, 64, 1200, logit_std=4.0, ignore_frac=0.1)
