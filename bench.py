@@ -335,6 +335,9 @@ def main():
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the small-LM, large-vocab and embedding-heavy CE timings")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="time the CE sequence at the 8B-class shard over N and H instead "
+                         "(one JSON line per shape) and exit")
     ap.add_argument("--reduce-mfma", metavar="COUNTER_CSV",
                     help="summarise a rocprofv3 --pmc run of this script with MFMA_COUNTERS and "
                          "--kernel-trace into profiles/ and exit (no GPU needed)")
@@ -379,6 +382,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.shape_sweep:
+        shape_sweep(torch, vp, dev)
+        return
 
     t0 = time.time()
     inp = vp_inputs.make_inputs("shard_8b")
@@ -543,6 +549,68 @@ def main():
             result["embedding_heavy_backward"]["cpu_baseline"] = cpu_baseline_embed_bwd(
                 embed_inputs["ids"], embed_inputs["dout"])
     print(json.dumps(result))
+
+
+SWEEP_SHAPES = [(1024, 4096), (2048, 4096), (4096, 4096), (8192, 4096), (16384, 4096),
+                (32768, 4096), (8192, 1024), (8192, 2048), (8192, 8192)]
+
+
+def shape_sweep(torch, vp, dev, Vs=16032, T=8, steps=10, warmup=3):
+    """Step time of shard 0's forward, the combine over T = 8 and shard 0's backward at the
+    8B-class shard width (Vs = 16032) over token counts N and hidden sizes H.  Inputs as the
+    8B-class workload: X ~ N(0, 1), W ~ N(0, 0.02) in bf16, uniform targets; the other
+    shards' statistics are synthetic (only their count matters to the combine's time).
+    Each shape is gated on shard 0's statistics of 32 sampled tokens against a plain fp32
+    evaluation of their logits (max, sum-exp about it, target logit)."""
+    for N, H in SWEEP_SHAPES:
+        g = torch.Generator(device=dev).manual_seed(N * 7 + H)
+        x = torch.randn((N, H), device=dev, generator=g).bfloat16()
+        w = (0.02 * torch.randn((Vs, H), device=dev, generator=g)).bfloat16()
+        y = torch.randint(0, Vs * T, (N,), device=dev, generator=g)
+        m = torch.full((T, N), 1.0, device=dev)
+        s = torch.full((T, N), 1000.0, device=dev)
+        zy = torch.zeros((T, N), device=dev)
+        loss, lse = torch.empty(N, device=dev), torch.empty(N, device=dev)
+        mean = torch.empty(1, device=dev)
+        dx, dw = torch.empty((N, H), device=dev), torch.empty((Vs, H), device=dev)
+        wf = vp.alloc_workspace(vp.vp_lmhead_ce_fwd_workspace(N, H, 0, Vs), dev)
+        wb = vp.alloc_workspace(vp.vp_lmhead_ce_bwd_workspace(N, H, 0, Vs), dev)
+
+        def step():
+            vp.vp_lmhead_ce_fwd(x, w, y, 0, Vs, m[0], s[0], zy[0], workspace=wf)
+            vp.vp_ce_combine(m, s, zy, y, loss=loss, lse=lse, loss_mean=mean)
+            vp.vp_lmhead_ce_bwd(x, w, y, lse, 0, Vs, 1.0 / N, dx=dx, dw=dw, workspace=wb)
+
+        step()
+        torch.cuda.synchronize()
+        rows = torch.randperm(N, generator=torch.Generator().manual_seed(N))[:32].to(dev)
+        z = x[rows].float() @ w.float().t()
+        zm = z.max(dim=1).values
+        zs = torch.exp(z - zm[:, None]).sum(dim=1)
+        yr = y[rows]
+        own = yr < Vs
+        zt = torch.where(own, z.gather(1, yr.clamp(max=Vs - 1)[:, None])[:, 0], torch.zeros_like(zm))
+        err = max(float((m[0, rows] - zm).abs().max()), float((zy[0, rows] - zt).abs().max()),
+                  float(((s[0, rows] - zs).abs() / zs).max()))
+        if not err <= 2e-3:
+            print(json.dumps({"N": N, "H": H, "error": "statistics check failed", "err": err}))
+            sys.exit(1)
+        for _ in range(warmup):
+            step()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        print(json.dumps({"N": N, "H": H, "Vs": Vs, "ms": round(ms, 4),
+                          "tokens_per_s": round(N / ms * 1e3), "stats_check_err": err,
+                          "frac": round(6.0 * N * Vs * H / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4)}),
+              flush=True)
+        del x, w, dx, dw, wf, wb, z
+        torch.cuda.empty_cache()
 
 
 def yardsticks(torch, dev, stream, N, H, Vs, reps=10):
