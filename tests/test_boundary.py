@@ -244,3 +244,30 @@ def test_product_does_not_reference_oracle():
         if os.path.isfile(path) and path.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
             txt = open(path).read()
             assert not re.search(r"\boracle\b", txt), path
+
+
+def test_binding_refuses_host_and_mismatched_tensors():
+    """Without a GPU: the binding refuses host tensors (their pointers would reach the
+    kernels), wrong dtypes, a host workspace, tensors spread over two devices and
+    mis-shaped buffers, each before the library is called."""
+    import torch
+    import vocab_lm_head_amd as vp
+    from vocab_lm_head_amd import _lib
+    n, h, vs = 16, 8, 24
+    x = torch.zeros((n, h), dtype=torch.bfloat16)
+    w = torch.zeros((vs, h), dtype=torch.bfloat16)
+    y = torch.zeros(n, dtype=torch.int64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        vp.vp_lmhead_ce_fwd(x, w, y, 0, vs)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        vp.vp_embed_fwd(y, w, 0, vs)
+    with pytest.raises(TypeError):
+        vp.vp_lmhead_ce_fwd(x.float(), w, y, 0, vs)
+    with pytest.raises(TypeError):
+        vp.vp_embed_fwd(y.int(), w, 0, vs)
+    with pytest.raises(ValueError, match="workspace"):
+        _lib._workspace(torch.zeros(64, dtype=torch.uint8), 64, "cpu")
+    with pytest.raises(ValueError, match="one GPU"):
+        _lib._same_device(x, torch.zeros(1, device="meta"))
+    with pytest.raises(ValueError):
+        _lib._shape(torch.zeros((n - 1, h)), (n, h), "dx")
