@@ -146,3 +146,32 @@ def test_shard_8b_against_golden(vp):
     log(f"  stored logits (24 rows): max abs err {err:.2e}")
     assert err <= 2e-3
     sampled_grads({"grads": {0: grads}}, 0, x, w, y, gold["lse"], lo, g, r)
+
+
+def _sweep_cases():
+    """Seeded shapes: odd N (1-2500), H a multiple of 8 (8-1024), Vs 1-5000 with T 1-4,
+    so that stored rows are padded by 0-3 columns and the gradient GEMMs run single-pass
+    or split over K; alternating one-read and two-pass statistics."""
+    r = np.random.default_rng(4242)
+    out = []
+    for i in range(12):
+        T = int(r.integers(1, 5))
+        N = int(r.integers(1, 2501))
+        H = 8 * int(r.integers(1, 129))
+        Vs = int(r.integers(1, 5001))
+        out.append((i, N, H, Vs, T, bool(i % 2)))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep_cases(),
+                         ids=lambda c: f"{c[0]}-N{c[1]}-H{c[2]}-Vs{c[3]}-T{c[4]}-{'two' if c[5] else 'one'}")
+def test_random_shape(vp, case):
+    i, N, H, Vs, T, two_pass = case
+    r = np.random.default_rng(5000 + i)
+    V = Vs * T
+    xb = vp_inputs.f32_to_bf16_bits(r.standard_normal((N, H)).astype(np.float32))
+    wb = vp_inputs.f32_to_bf16_bits(
+        r.standard_normal((V, H)).astype(np.float32) * np.float32(3.0 / math.sqrt(H)))
+    y = r.integers(0, V, N).astype(np.int64)
+    y[r.random(N) < 0.1] = -100
+    _full_check(vp, xb, wb, y, T, two_pass, f"case {i}")
