@@ -25,7 +25,9 @@ Sources (the pages this method is described on):
 * Glossary "Tensor Parallelism" -- column-parallel linear: each shard's input
   gradient is a partial sum over shards.
 
-Parity pins for every function live in ``tests/test_oracle.py``.
+Parity pins for every function live in ``tests/oracle_pins.py`` (run by
+``tests/test_oracle.py``; ``tests/test_oracle_mutations.py`` checks that they
+catch planted mistakes).
 """
 from __future__ import annotations
 
@@ -38,7 +40,7 @@ __all__ = [
     "embed_shard_grad_rows", "logits",
     "shard_stats", "shard_sumexp", "combine_triples", "pages_sharded_ce", "dense_ce",
     "dense_dlogits", "shard_grads", "mean_scale", "lse_dense_chunked",
-    "shard_stats_chunked", "dz_rows", "dz_cols",
+    "shard_stats_chunked", "dz_rows", "dz_cols", "shard_grads_chunked",
 ]
 
 
@@ -337,3 +339,29 @@ def dz_cols(x: np.ndarray, w_rows: np.ndarray, vocab_ids, targets, lse,
     p -= (t[:, None] == ids[None, :]).astype(np.float64)
     p[t == ignore_index] = 0.0
     return p * scale
+
+
+def shard_grads_chunked(x: np.ndarray, w_shard: np.ndarray, targets, lse, start: int,
+                        scale: float, ignore_index: int = DEFAULT_IGNORE_INDEX,
+                        chunk: int = 512):
+    """``shard_grads`` of one shard over all tokens, with its dlogits formed token-chunked.
+
+    For each chunk of tokens, ``dz_rows`` gives the shard's columns of dlogits from the
+    tokens' full-vocabulary lse; that chunk's rows of dX_r = dz_r W_r are stored and its
+    dz_r^T X is added into dW_r = sum over chunks (the column-parallel partial and the local
+    weight gradient of the interview note's backward remark).  Chunking only bounds host
+    memory; it changes no term of either sum.  Returns fp64 (dX_r [N, H], dW_r [Vs, H]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_shard, dtype=np.float64)
+    t = np.asarray(targets, dtype=np.int64)
+    ls = np.asarray(lse, dtype=np.float64)
+    n = x.shape[0]
+    dx = np.empty((n, w.shape[1]))
+    dw = np.zeros(w.shape)
+    for a in range(0, n, chunk):
+        dz = dz_rows(x[a:a + chunk], w, t[a:a + chunk], ls[a:a + chunk], start, scale,
+                     ignore_index)
+        dx[a:a + chunk] = np.matmul(dz, w)
+        dw += np.matmul(dz.T, x[a:a + chunk])
+    return dx, dw

@@ -388,6 +388,10 @@ def pin_sliced_helpers(o):
                        rtol=0, atol=1e-15)
     cols = np.array([0, 40, 95, 63])
     assert np.allclose(o.dz_cols(x, w[cols], cols, y, lse, g), dz[:, cols], rtol=0, atol=1e-15)
+    # whole-shard gradients from token chunks (a ragged last chunk) == the dense ones
+    dxr, dwr = o.shard_grads(x, w[lo:hi], dz[:, lo:hi])
+    dxc, dwc = o.shard_grads_chunked(x, w[lo:hi], y, lse, lo, g, chunk=16)
+    assert np.allclose(dxc, dxr, rtol=0, atol=1e-14) and np.allclose(dwc, dwr, rtol=0, atol=1e-14)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

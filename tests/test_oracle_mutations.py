@@ -60,6 +60,10 @@ MUTATIONS = [
     ("np.add.at(out, ids[own] - start, g[own])", "np.add.at(out, np.minimum(ids[own], end - start - 1), g[own])"),
     # lookup gradient: the shard's first id dropped
     ("own = (ids >= start) & (ids < end)\n    np.add.at", "own = (ids > start) & (ids < end)\n    np.add.at"),
+    # chunked shard gradients: each chunk overwrites dW instead of adding to it
+    ("        dw += np.matmul(dz.T, x[a:a + chunk])", "        dw = np.matmul(dz.T, x[a:a + chunk])"),
+    # chunked shard gradients: dX rows of a chunk stored from the wrong operand
+    ("        dx[a:a + chunk] = np.matmul(dz, w)", "        dx[a:a + chunk] = np.matmul(dz, w[::-1])"),
     # lookup gradient rows: id compared without the shard start
     ("sel = np.nonzero(ids == start + int(r))[0]", "sel = np.nonzero(ids == int(r))[0]"),
 ]
