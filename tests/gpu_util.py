@@ -120,6 +120,38 @@ def sampled_grads(out, t, x, w_shard, y, lse_ref, start, g, rng, k_rows=24, k_co
     assert_grad_close(host(out["grads"][t][1][cols]), dzc.T @ x, f"dW_{t} ({cols.size} rows)")
 
 
+def _rel_max_device(got_d, ref, rows_per_piece=2048):
+    """max|got - ref| / max|ref| over whole tensors, with ``got_d`` (a GPU tensor) brought
+    to the host a slab of rows at a time (a full-size gradient in fp64 would double host
+    memory)."""
+    num = den = 0.0
+    finite = True
+    for a in range(0, ref.shape[0], rows_per_piece):
+        g = got_d[a:a + rows_per_piece].detach().cpu().numpy().astype(np.float64)
+        r = ref[a:a + rows_per_piece]
+        finite = finite and bool(np.isfinite(g).all())
+        num = max(num, float(np.abs(g - r).max()))
+        den = max(den, float(np.abs(r).max()))
+    return (num / den if den > 0 else num), finite
+
+
+def full_grads(out, t, x, w_shard, y, lse_ref, start, g):
+    """Every element of shard t's dX partial and dW against the oracle (its dlogits formed
+    token-chunked from the tokens' fp64 lse), with the bar's per-tensor denominator taken
+    over the whole oracle tensor."""
+    import time
+    t0 = time.time()
+    dx_ref, dw_ref = oracle.shard_grads_chunked(x, w_shard, y, lse_ref, start, g)
+    log(f"  oracle dX/dW of shard {t} ({x.shape[0]} x {w_shard.shape[0]} x {x.shape[1]}): "
+        f"{time.time() - t0:.1f} s")
+    for name, got_d, ref in (("dX", out["grads"][t][0], dx_ref), ("dW", out["grads"][t][1], dw_ref)):
+        e, finite = _rel_max_device(got_d, ref)
+        log(f"  {name}_{t} (all {ref.shape[0]} x {ref.shape[1]}): max|d|/max|ref| {e:.3e} "
+            f"(bar {GRAD_RTOL})")
+        assert finite, f"{name}_{t}: non-finite values"
+        assert e <= GRAD_RTOL, f"{name}_{t}: relative error {e} > {GRAD_RTOL}"
+
+
 def embed_bwd_run(vp, ids, dout_bits, lo, hi, dw0):
     """vp_embed_bwd on the GPU, adding into a device copy of dw0."""
     dw = torch.from_numpy(np.ascontiguousarray(dw0, dtype=np.float32)).cuda()
