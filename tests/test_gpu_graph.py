@@ -150,3 +150,53 @@ def test_side_stream_and_graph_replays(vp):
         torch.cuda.synchronize()
         _same(_snapshot(step), want, f"replay {k} (inputs {seed})")
         log(f"  replay {k} (inputs {seed}): bit-identical to the eager step")
+
+
+def test_explicit_stream_argument(vp):
+    """Calls given ``stream=`` a side stream that is not the current one, with the wrappers
+    allocating their own workspaces and outputs.  Those are allocated on the side stream, so
+    the caching allocator cannot hand a freed workspace to work queued on the current stream
+    while the side stream's kernels still use it: work on the current stream right after
+    the calls (allocations of the same sizes, filled with garbage) must not change the
+    results, which equal the eager ones bit for bit."""
+    import torch
+    inp = vp_inputs.make_inputs("small_lm")
+    step = _Step(vp, inp)
+    _load(step, 105)
+    wl = step.wl
+    a0, b0 = step.rng[0]
+    w0 = step.w[a0:b0]
+    # eager on the current stream, library-allocated workspaces
+    m, s, zy = (torch.empty((step.T, step.N), device="cuda") for _ in range(3))
+    for t, (a, b) in enumerate(step.rng):
+        vp.vp_lmhead_ce_fwd(step.x, step.w[a:b], step.y, a, b, m[t], s[t], zy[t])
+    loss, lse, mean = vp.vp_ce_combine(m, s, zy, step.y)
+    dx, dw = vp.vp_lmhead_ce_bwd(step.x, w0, step.y, lse, a0, b0, step.g)
+    dwe = vp.vp_embed_bwd(step.ids, step.dout, a0, b0)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (m, s, zy, loss, lse, mean, dx, dw, dwe)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    m2, s2, zy2 = (torch.empty((step.T, step.N), device="cuda") for _ in range(3))
+    for t, (a, b) in enumerate(step.rng):
+        vp.vp_lmhead_ce_fwd(step.x, step.w[a:b], step.y, a, b, m2[t], s2[t], zy2[t], stream=side)
+    loss2, lse2, mean2 = vp.vp_ce_combine(m2, s2, zy2, step.y, stream=side)
+    dx2, dw2 = vp.vp_lmhead_ce_bwd(step.x, w0, step.y, lse2, a0, b0, step.g, stream=side)
+    dwe2 = vp.vp_embed_bwd(step.ids, step.dout, a0, b0, stream=side)
+    # the current stream reuses whatever its pool holds, at the workspaces' sizes
+    vs = b0 - a0
+    junk = [torch.empty(vp.vp_lmhead_ce_bwd_workspace(step.N, step.H, a0, b0), dtype=torch.uint8,
+                        device="cuda").fill_(0xFF),
+            torch.empty(vp.vp_lmhead_ce_fwd_workspace(step.N, step.H, a0, b0), dtype=torch.uint8,
+                        device="cuda").fill_(0xFF),
+            torch.empty(vp.vp_embed_bwd_workspace(wl.embed_N, step.H, a0, b0), dtype=torch.uint8,
+                        device="cuda").fill_(0xFF),
+            torch.full((vs, step.H), float("nan"), device="cuda")]
+    side.synchronize()
+    torch.cuda.synchronize()
+    got = (m2, s2, zy2, loss2, lse2, mean2, dx2, dw2, dwe2)
+    for k, (u, v) in enumerate(zip(got, want)):
+        assert torch.equal(u, v), f"output {k} differs with stream= a side stream"
+    del junk
+    log("  every output bit-identical with stream= a side stream")

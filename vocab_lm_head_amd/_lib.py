@@ -1,8 +1,14 @@
 """ctypes binding of ``libvplmhead.so`` -- argument marshalling only.
 
 Each function takes torch tensors that already live on the GPU, checks dtypes
-and shapes, passes ``data_ptr()`` values and the current HIP stream to the C
-entry point of the same name, and raises ``VPError`` on a non-zero status.
+and shapes, passes ``data_ptr()`` values and a HIP stream (the ``stream``
+argument, else the current stream of the tensors' GPU) to the C entry point of
+the same name, and raises ``VPError`` on a non-zero status.
+
+Buffers a wrapper allocates itself (a workspace the caller did not pass, default
+outputs) are allocated while that stream is current, so that torch's caching
+allocator files them under the stream the kernels use: a temporary workspace
+freed on return cannot be handed to other work before those kernels are done.
 Every step of the computation runs in the library's HIP kernels; nothing here
 computes a result.  If the library has not been built, importing this module
 fails loudly -- there is no fallback.
@@ -10,6 +16,7 @@ fails loudly -- there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -84,6 +91,18 @@ def _stream(stream, device) -> int:
     return s.cuda_stream
 
 
+def _on_stream(fn):
+    """Run a wrapper with its ``stream`` argument (when given) as the current stream, so
+    that every tensor it allocates belongs to that stream's memory pool."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kwargs)
+    return call
+
+
 def _same_device(*tensors):
     devs = {t.device for t in tensors if t is not None}
     if len(devs) > 1:
@@ -137,6 +156,7 @@ def vp_padded_vocab(V: int, T: int, multiple: int = 128) -> int:
     return out.value
 
 
+@_on_stream
 def vp_embed_fwd(ids, w_shard, vocab_start: int, vocab_end: int, out=None, stream=None):
     """Masked lookup of one shard: out[i] = w_shard[ids[i]-start] if owned, else 0."""
     _need(ids, torch.int64, 1, "ids")
@@ -159,6 +179,7 @@ def vp_embed_bwd_workspace(n: int, h: int, vocab_start: int, vocab_end: int) -> 
     return int(lib.vp_embed_bwd_workspace(n, h, vocab_start, vocab_end))
 
 
+@_on_stream
 def vp_embed_bwd(ids, dout, vocab_start: int, vocab_end: int, dw=None, workspace=None, stream=None):
     """Lookup weight gradient of one shard, ADDED to dw (fp32 [Vs, h]; zeros if not given):
     dw[ids[i] - start] += dout[i] for owned ids."""
@@ -195,6 +216,7 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+@_on_stream
 def vp_lmhead_ce_fwd(hidden, w_shard, targets, vocab_start: int, vocab_end: int,
                      m_local=None, s_local=None, zy_local=None, workspace=None, stream=None):
     """Per-token (local max, local sum-exp, owned target logit) of one shard, fp32 [n] each."""
@@ -223,6 +245,7 @@ def vp_lmhead_ce_fwd(hidden, w_shard, targets, vocab_start: int, vocab_end: int,
     return tuple(outs)
 
 
+@_on_stream
 def vp_ce_combine(m, s, zy, targets, ignore_index: int = DEFAULT_IGNORE_INDEX,
                   loss=None, lse=None, loss_mean=None, stream=None):
     """Merge [T, n] statistics -> (loss [n], lse [n], loss_mean [1]), fp32."""
@@ -247,6 +270,7 @@ def vp_ce_combine(m, s, zy, targets, ignore_index: int = DEFAULT_IGNORE_INDEX,
     return loss, lse, loss_mean
 
 
+@_on_stream
 def vp_lmhead_ce_bwd(hidden, w_shard, targets, lse, vocab_start: int, vocab_end: int,
                      grad_scale: float, ignore_index: int = DEFAULT_IGNORE_INDEX,
                      dx=None, dw=None, workspace=None, stream=None):
@@ -284,6 +308,7 @@ def logits_ld(vs: int) -> int:
     return -(-int(vs) // 4) * 4
 
 
+@_on_stream
 def vp_lmhead_logits(hidden, w_shard, vocab_start: int, vocab_end: int, logits=None, stream=None):
     """fp32 logits [n, ld] of one shard (columns past Vs are zero)."""
     _need(hidden, torch.bfloat16, 2, "hidden")
@@ -304,6 +329,7 @@ def vp_lmhead_logits(hidden, w_shard, vocab_start: int, vocab_end: int, logits=N
     return logits
 
 
+@_on_stream
 def vp_logits_ce_stats(logits, targets, vocab_start: int, vocab_end: int, m_ref=None,
                        m_local=None, s_local=None, zy_local=None, stream=None):
     """(m, s, zy) fp32 [n] of one shard from its stored logits; with m_ref, s is taken
@@ -329,6 +355,7 @@ def vp_logits_ce_stats(logits, targets, vocab_start: int, vocab_end: int, m_ref=
     return tuple(outs)
 
 
+@_on_stream
 def vp_ce_max(m, out=None, stream=None):
     """Per-token maximum over the T rows of m [T, n]."""
     _need(m, torch.float32, 2, "m")
@@ -341,6 +368,7 @@ def vp_ce_max(m, out=None, stream=None):
     return out
 
 
+@_on_stream
 def vp_logits_ce_bwd(logits, hidden, w_shard, targets, lse, vocab_start: int, vocab_end: int,
                      grad_scale: float, ignore_index: int = DEFAULT_IGNORE_INDEX,
                      dx=None, dw=None, workspace=None, stream=None):
