@@ -279,12 +279,104 @@ def reduce_mfma(path, cmd):
     print("\n".join(lines))
 
 
+def _run_text(cmd, timeout=30):
+    """stdout of a command, or None if it is missing or fails (information only)."""
+    import subprocess
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return r.stdout if r.returncode == 0 else None
+
+
+def _read(path):
+    try:
+        with open(path) as fh:
+            return fh.read().strip()
+    except OSError:
+        return None
+
+
+def gpu_clock_and_driver():
+    """The GPU's clocks and driver as the system reports them: rocm-smi's current and
+    supported engine clocks and its driver version, the amdgpu module version, the ROCm
+    release; and the engine clock the CE GEMMs ran at under load, from the committed
+    counter summary (GRBM_GUI_ACTIVE over the kernels' durations) when it was taken on
+    the kernels as built."""
+    out = {"rocm": _read("/opt/rocm/.info/version"),
+           "amdgpu_module_version": _read("/sys/module/amdgpu/version")}
+    txt = _run_text(["rocm-smi", "--showclocks", "--showdriverversion", "--json"])
+    if txt:
+        try:
+            info = json.loads(txt)
+            for card, d in info.items():
+                if not isinstance(d, dict):
+                    continue
+                if card == "system":
+                    out["driver_version"] = d.get("Driver version")
+                    continue
+                out.setdefault("clocks_at_query", {})[card] = {
+                    k: v for k, v in d.items() if "clock" in k.lower() or "sclk" in k.lower()}
+        except (ValueError, AttributeError):
+            out["rocm_smi_raw"] = txt[:400]
+    levels = _run_text(["rocm-smi", "--showclkfrq"])
+    if levels:
+        out["sclk_levels"] = " ".join(l.strip() for l in levels.splitlines()
+                                      if "Mhz" in l or "MHz" in l)[:400]
+    try:
+        txt = open(MFMA_PROFILE).read()
+        h = re.search(r"^kernel_source_hash: (\w+)", txt, re.M)
+        if h and h.group(1) == kernel_source_hash():
+            clk = {}
+            for line in txt.splitlines():
+                f = line.split()
+                if len(f) >= 5 and f[0].isdigit() and "Epilogue" in line:
+                    clk.setdefault(f[4], []).append(float(f[2]))
+            out["gemm_clock_under_load_GHz"] = {k: round(sum(v) / len(v), 3) for k, v in clk.items()}
+            out["gemm_clock_source"] = "profiles/mfma_util_shard_8b.txt (rocprofv3 counters)"
+    except OSError:
+        pass
+    return out
+
+
 def device_info(torch, dev):
     """The device and software versions the numbers were taken on."""
     p = torch.cuda.get_device_properties(dev)
     return {"device": p.name, "arch": getattr(p, "gcnArchName", ""),
             "compute_units": p.multi_processor_count, "hbm_GiB": round(p.total_memory / 2**30, 1),
-            "hip": torch.version.hip, "torch": torch.__version__}
+            "hip": torch.version.hip, "torch": torch.__version__, **gpu_clock_and_driver()}
+
+
+def host_cpu_info():
+    """The host the oracle baseline ran on: CPU model, the cores visible to this process,
+    and NumPy's BLAS (library, version, threads) as threadpoolctl sees it."""
+    model = None
+    txt = _read("/proc/cpuinfo") or ""
+    m = re.search(r"^model name\s*:\s*(.+)$", txt, re.M)
+    if m:
+        model = m.group(1).strip()
+    try:
+        import threadpoolctl
+        blas = [{k: d.get(k) for k in ("internal_api", "version", "num_threads",
+                                         "threading_layer", "architecture", "filepath")}
+                for d in threadpoolctl.threadpool_info()]
+    except Exception:   # noqa: BLE001 -- information only
+        blas = None
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"), "numpy": np.__version__,
+            "blas": blas}
+
+
+def oracle_threads():
+    """Threads for the oracle's BLAS: every core this process may run on, except where the
+    environment sets the job's CPU share (OMP_NUM_THREADS, which a shared GPU host sets to
+    the cores allotted to one GPU's job); then that share."""
+    cores = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        cores = min(cores, int(env))
+    return cores
 
 
 def dev_bf16(torch, bits, dev):
@@ -297,7 +389,7 @@ def cpu_baseline(inp, sample_tokens: int):
 
     import oracle
     import vp_inputs
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores = oracle_threads()
     wl = inp.wl
     rng = np.random.default_rng(1234)
     rows = np.sort(rng.choice(wl.N, sample_tokens, replace=False))
@@ -318,7 +410,9 @@ def cpu_baseline(inp, sample_tokens: int):
         dz0 = oracle.dz_rows(x, w[0], y, lse, 0, g)                   # shard-0 backward
         dx0, dw0 = oracle.shard_grads(x, w[0], dz0)
         dt = time.perf_counter() - t0
+        host = host_cpu_info()   # inside the limits: the BLAS threads it actually used
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "host": host,
             "sample": f"{sample_tokens} of the {wl.N} tokens (seeded choice): shard-0 forward + "
                       f"combine of 8 shards + shard-0 backward, NumPy fp64, {dt:.1f} s"}
 
