@@ -55,7 +55,9 @@ typedef enum {
     VP_ERR_RANGE = -3,      /* vocab_end <= vocab_start, or t outside [0, T)    */
     VP_ERR_ALIGN = -4,      /* H % 8 != 0 or a pointer is misaligned           */
     VP_ERR_WORKSPACE = -5,  /* workspace pointer null or smaller than required */
-    VP_ERR_HIP = -6         /* the HIP runtime reported an error at launch     */
+    VP_ERR_HIP = -6,        /* the HIP runtime reported an error at launch     */
+    VP_ERR_SCRATCH = -7     /* the call needs more scratch than the fixed device buffer of
+                               the allocation-free entry point holds               */
 } vp_status;
 
 /* Human-readable name of a status code (static string, never null). */
@@ -146,6 +148,31 @@ int vp_lmhead_ce_fwd(const uint16_t *hidden, const uint16_t *w_shard, const int6
                      int64_t n, int64_t h, int64_t vocab_start, int64_t vocab_end,
                      float *m_local, float *s_local, float *zy_local,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the fixed device scratch buffer of vp_lmhead_ce_fwd_noalloc (64 MiB). */
+#define VP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * vp_lmhead_ce_fwd_noalloc -- vp_lmhead_ce_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, bit for bit, with the workspace taken from a
+ * fixed buffer of VP_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  Calls no allocator.  The caller still passes inputs and outputs
+ * (arguments as vp_lmhead_ce_fwd, without the workspace).
+ *   Limit: vp_lmhead_ce_fwd_workspace(n, h, vocab_start, vocab_end) must not exceed
+ *   VP_NOALLOC_SCRATCH_BYTES (e.g. n = 16384 tokens with a 19008-row shard needs 29.3 MB),
+ *   else VP_ERR_SCRATCH and nothing is launched.
+ *   Every call on one GPU uses that GPU's one buffer: calls that overlap in time on one GPU
+ *   (on different streams, or from different threads) race and must be serialised by the
+ *   caller.  The buffer needs no clearing: every byte a call reads it has written first.
+ *   The buffer of the stream's GPU is looked up on the first call on that GPU (the device
+ *   is switched for that lookup and restored).
+ * n == 0: no-op.  Errors: NULL, SHAPE, RANGE, ALIGN, SCRATCH, HIP.
+ */
+int vp_lmhead_ce_fwd_noalloc(const uint16_t *hidden, const uint16_t *w_shard,
+                             const int64_t *targets, int64_t n, int64_t h,
+                             int64_t vocab_start, int64_t vocab_end,
+                             float *m_local, float *s_local, float *zy_local, hipStream_t stream);
 
 /*
  * vp_ce_combine -- merge T shards' statistics into the loss; stands in for the

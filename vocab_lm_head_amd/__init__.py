@@ -11,6 +11,8 @@ from ._lib import (  # noqa: F401
     vp_lmhead_ce_bwd_workspace, vp_lmhead_ce_fwd, vp_lmhead_ce_fwd_workspace, vp_padded_vocab,
     vp_shard_range,
 )
+# the forward for callers that cannot allocate (fixed per-GPU scratch, no workspace)
+from ._lib import NOALLOC_SCRATCH_BYTES, VP_ERR_SCRATCH, vp_lmhead_ce_fwd_noalloc  # noqa: F401
 # materialised-logits comparator (beside the fused path, to measure what it saves)
 from ._lib import (  # noqa: F401
     logits_ld, vp_ce_max, vp_lmhead_logits, vp_logits_ce_bwd, vp_logits_ce_stats,

@@ -26,6 +26,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("VP_LMHEAD_LIB") or os.path.join(_HERE, "libvplmhead.so")
 
 VP_OK = 0
+VP_ERR_SCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 64 << 20   # VP_NOALLOC_SCRATCH_BYTES of the header
 DEFAULT_IGNORE_INDEX = -100
 
 # symbol -> (restype, argtypes); the names and order follow include/vp_lmhead.h
@@ -42,6 +44,7 @@ SIGNATURES = {
     "vp_embed_bwd": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "vp_lmhead_ce_fwd_workspace": (_SZ, [_I64, _I64, _I64, _I64]),
     "vp_lmhead_ce_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "vp_lmhead_ce_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
     "vp_ce_combine": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I64, _P, _P, _P, _P]),
     "vp_lmhead_ce_bwd_workspace": (_SZ, [_I64, _I64, _I64, _I64]),
     "vp_lmhead_ce_bwd": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
@@ -243,6 +246,28 @@ def vp_lmhead_ce_fwd(hidden, w_shard, targets, vocab_start: int, vocab_end: int,
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream, dev)), "vp_lmhead_ce_fwd")
     return tuple(outs)
+
+
+@_on_stream
+def vp_lmhead_ce_fwd_noalloc(hidden, w_shard, targets, vocab_start: int, vocab_end: int,
+                             m_local, s_local, zy_local, stream=None):
+    """vp_lmhead_ce_fwd with the library's fixed per-GPU scratch instead of a workspace: the
+    caller passes the three fp32 [n] outputs and nothing is allocated."""
+    _need(hidden, torch.bfloat16, 2, "hidden")
+    _need(w_shard, torch.bfloat16, 2, "w_shard")
+    _need(targets, torch.int64, 1, "targets")
+    n, h = hidden.shape
+    if w_shard.shape != (vocab_end - vocab_start, h) or targets.shape[0] != n:
+        raise ValueError("shape mismatch between hidden, w_shard, targets and the vocab range")
+    for t in (m_local, s_local, zy_local):
+        _need(t, torch.float32, 1, "statistics output")
+        _shape(t, (n,), "statistics output")
+    _same_device(hidden, w_shard, targets, m_local, s_local, zy_local)
+    _check(lib.vp_lmhead_ce_fwd_noalloc(_ptr(hidden), _ptr(w_shard), _ptr(targets), n, h,
+                                        int(vocab_start), int(vocab_end), _ptr(m_local),
+                                        _ptr(s_local), _ptr(zy_local), _stream(stream, hidden.device)),
+           "vp_lmhead_ce_fwd_noalloc")
+    return m_local, s_local, zy_local
 
 
 @_on_stream

@@ -49,6 +49,9 @@ const char *vp_status_string(int status) {
         case VP_ERR_ALIGN: return "VP_ERR_ALIGN: h must be a multiple of 8 and tensors 16-byte aligned";
         case VP_ERR_WORKSPACE: return "VP_ERR_WORKSPACE: workspace missing or too small";
         case VP_ERR_HIP: return "VP_ERR_HIP: the HIP runtime reported a launch error";
+        case VP_ERR_SCRATCH:
+            return "VP_ERR_SCRATCH: the call needs more than the allocation-free entry point's "
+                   "fixed scratch buffer (VP_NOALLOC_SCRATCH_BYTES); use the workspace form";
         default: return "unknown vp_status";
     }
 }
@@ -127,6 +130,24 @@ int vp_lmhead_ce_fwd(const uint16_t *hidden, const uint16_t *w_shard, const int6
         return VP_ERR_WORKSPACE;
     return hip_status(vp::launch_ce_fwd(hidden, w_shard, targets, n, h, vocab_start, vs, m_local,
                                         s_local, zy_local, workspace, stream));
+}
+
+int vp_lmhead_ce_fwd_noalloc(const uint16_t *hidden, const uint16_t *w_shard,
+                             const int64_t *targets, int64_t n, int64_t h, int64_t vocab_start,
+                             int64_t vocab_end, float *m_local, float *s_local, float *zy_local,
+                             hipStream_t stream) {
+    static_assert(VP_NOALLOC_SCRATCH_BYTES == vp::kNoallocScratchBytes, "one scratch size");
+    int st = check_shard(n, h, vocab_start, vocab_end);
+    if (st != VP_OK) return st;
+    if (n == 0) return VP_OK;
+    if (!hidden || !w_shard || !targets || !m_local || !s_local || !zy_local) return VP_ERR_NULL;
+    if (!aligned(hidden, 16) || !aligned(w_shard, 16) || !aligned(targets, 8) ||
+        !aligned(m_local, 4) || !aligned(s_local, 4) || !aligned(zy_local, 4))
+        return VP_ERR_ALIGN;
+    const int64_t vs = vocab_end - vocab_start;
+    if (vp::fwd_workspace(n, vs).bytes > vp::kNoallocScratchBytes) return VP_ERR_SCRATCH;
+    return hip_status(vp::launch_ce_fwd_noalloc(hidden, w_shard, targets, n, h, vocab_start, vs,
+                                                m_local, s_local, zy_local, stream));
 }
 
 int vp_ce_combine(const float *m, const float *s, const float *zy, const int64_t *targets,

@@ -9,9 +9,16 @@
 //   (m, s) <- (max(m, m'), s e^(m - max) + s' e^(m' - max)),
 // which is exact in real arithmetic; the [N, Vs] logits never leave registers.
 #include <algorithm>
+#include <mutex>
 
 #include "gemm.hpp"
 #include "launch.hpp"
+
+// Fixed scratch of the allocation-free forward (vp_lmhead_ce_fwd_noalloc): each GPU the
+// library runs on holds one copy, at an address of its own, until the process ends.  In
+// host code this name is not a device address; the address of each GPU's copy comes from
+// hipGetSymbolAddress with that GPU current (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[vp::kNoallocScratchBytes];
 
 namespace vp {
 
@@ -218,6 +225,47 @@ hipError_t launch_ce_fwd(const uint16_t *x, const uint16_t *w, const int64_t *ta
                            fw.splits, n, fw.splits, m_out, s_out, zy_out, (int64_t)0);
     }
     return hipGetLastError();
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];   // per device: its copy of `scratch`, once looked up
+
+// Device address of the scratch copy on the GPU that `stream` runs on; looked up once per
+// GPU, with that GPU current (the caller's current device is restored).
+hipError_t noalloc_scratch(hipStream_t stream, void **out) {
+    hipDevice_t dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (back != hipSuccess) return back;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_ce_fwd_noalloc(const uint16_t *x, const uint16_t *w, const int64_t *targets,
+                                 int64_t n, int64_t h, int64_t start, int64_t vs, float *m_out,
+                                 float *s_out, float *zy_out, hipStream_t stream) {
+    void *ws = nullptr;
+    const hipError_t e = noalloc_scratch(stream, &ws);
+    if (e != hipSuccess) return e;
+    return launch_ce_fwd(x, w, targets, n, h, start, vs, m_out, s_out, zy_out, ws, stream);
 }
 
 }  // namespace vp

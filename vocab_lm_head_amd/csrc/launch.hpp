@@ -51,6 +51,13 @@ hipError_t launch_ce_fwd(const uint16_t *x, const uint16_t *w, const int64_t *ta
                          int64_t h, int64_t start, int64_t vs, float *m_out, float *s_out,
                          float *zy_out, void *ws, hipStream_t stream);
 
+// the forward with its workspace in the library's fixed per-device scratch buffer
+// (caller has checked fwd_workspace(n, vs).bytes <= kNoallocScratchBytes)
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+hipError_t launch_ce_fwd_noalloc(const uint16_t *x, const uint16_t *w, const int64_t *targets,
+                                 int64_t n, int64_t h, int64_t start, int64_t vs, float *m_out,
+                                 float *s_out, float *zy_out, hipStream_t stream);
+
 hipError_t launch_ce_combine(const float *m, const float *s, const float *zy,
                              const int64_t *targets, int64_t n, int T, int64_t ignore_index,
                              float *loss, float *lse, float *loss_mean, hipStream_t stream);
