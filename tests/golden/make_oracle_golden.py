@@ -14,6 +14,11 @@ in ``oracle_<workload>.npz`` next to this script.  The GPU tests regenerate
 the same input bits from the same seeds and derive everything else they
 compare (statistics of shard 0, sampled rows of dX and dW) from these values
 with the oracle at test time.
+
+``sweep`` writes ``oracle_sweep.npz`` for the benchmark's scaling sweep (shard 0 of
+width 16032 at nine (N, H) shapes, the other seven shards given as fixed statistics):
+per shape, every token's loss (fp64) and the oracle's dX and dW on the rows
+``vp_inputs.sweep_samples`` names (stored as fp32; the gate's bar is relative 1e-2).
 """
 from __future__ import annotations
 
@@ -77,12 +82,34 @@ def golden_small_lm():
     return _dense_chunked(_f64(inp.x), _f64(inp.w), inp.targets, chunk=1024)
 
 
+def golden_sweep(Vs=16032, T=8):
+    out = {}
+    for N, H in vp_inputs.SWEEP_SHAPES:
+        xb, wb, y = vp_inputs.sweep_inputs(N, H, Vs, T)
+        x, w = _f64(xb), _f64(wb)
+        m0, s0, zy0 = oracle.shard_stats_chunked(x, w, y, 0, chunk=1024)
+        ones = np.ones(N)
+        loss, lse, _ = oracle.combine_triples(
+            np.stack([m0] + [ones] * (T - 1)), np.stack([s0] + [1000.0 * ones] * (T - 1)),
+            np.stack([zy0] + [0.0 * ones] * (T - 1)), y)
+        g = 1.0 / N
+        rows, cols = vp_inputs.sweep_samples(N, H, y, Vs)
+        key = f"{N}x{H}"
+        out[f"{key}_loss"] = loss
+        out[f"{key}_dx"] = (oracle.dz_rows(x[rows], w, y[rows], lse[rows], 0, g) @ w).astype(np.float32)
+        out[f"{key}_dw"] = (oracle.dz_cols(x, w[cols], cols, y, lse, g).T @ x).astype(np.float32)
+        print(f"  sweep {key} done", flush=True)
+    out["mean"] = np.array(0.0)   # (no single mean: one loss vector per shape)
+    return out
+
+
 MAKERS = {"shard_8b": golden_shard_8b, "large_vocab": golden_large_vocab,
-          "embedding_heavy": golden_embedding_heavy, "small_lm": golden_small_lm}
+          "embedding_heavy": golden_embedding_heavy, "small_lm": golden_small_lm,
+          "sweep": golden_sweep}
 
 
 def main(names):
-    for name in names or list(MAKERS):
+    for name in names or [k for k in MAKERS if k != "sweep"]:
         t = time.time()
         out = MAKERS[name]()
         path = os.path.join(HERE, f"oracle_{name}.npz")

@@ -36,7 +36,7 @@ import numpy as np
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
     "zipf_ids", "Workload", "WORKLOADS", "make_inputs", "Inputs",
-    "synthetic_triples",
+    "synthetic_triples", "SWEEP_SHAPES", "sweep_inputs",
 ]
 
 
@@ -320,3 +320,32 @@ def synthetic_triples(name: str, targets: np.ndarray):
         own = owner == r
         zy[r, own] = m[r, own] - gap[r - 1, own]
     return m, s, zy
+
+
+# ----------------------------------------------------------------------------
+# the benchmark's scaling sweep at the 8B-class shard width
+# ----------------------------------------------------------------------------
+SWEEP_SHAPES = [(1024, 4096), (2048, 4096), (4096, 4096), (8192, 4096), (16384, 4096),
+                (32768, 4096), (8192, 1024), (8192, 2048), (8192, 8192)]
+
+
+def sweep_inputs(N: int, H: int, Vs: int = 16032, T: int = 8):
+    """Inputs of one scaling-sweep shape: X ~ N(0, 1) [N, H] and shard 0's W ~ N(0, 0.02)
+    [Vs, H], both rounded to bf16 bits, and targets uniform over the T Vs ids, from one
+    PCG64 generator seeded N * 7 + H (X first, then W, then the targets).  The other shards
+    enter only through fixed statistics (m = 1, s = 1000, target logit 0)."""
+    rng = np.random.default_rng(N * 7 + H)
+    x = f32_to_bf16_bits(rng.standard_normal((N, H), dtype=np.float32))
+    w = f32_to_bf16_bits(np.float32(0.02) * rng.standard_normal((Vs, H), dtype=np.float32))
+    y = rng.integers(0, Vs * T, N).astype(np.int64)
+    return x, w, y
+
+
+def sweep_samples(N: int, H: int, y: np.ndarray, Vs: int = 16032):
+    """The rows the sweep's gate compares: 4 token rows of dX and 6 vocabulary rows of dW
+    (4 random ids and the first 2 owned targets), seeded by the shape."""
+    rows = np.sort(np.random.default_rng(N).choice(N, 4, replace=False))
+    own = y[y < Vs]
+    cols = np.unique(np.concatenate([np.random.default_rng(H).choice(Vs, 4, replace=False),
+                                     own[:2]])).astype(np.int64)
+    return rows, cols
