@@ -238,6 +238,40 @@ def reduce_pmc(fetch_csv, write_csv, cmd_fetch, cmd_write):
     print("\n".join(lines))
 
 
+def reduce_trace(path, name, title, cmd, last=5):
+    """Summarise a rocprofv3 --kernel-trace CSV into profiles/<name>.txt: per kernel (short
+    name and grid), the mean duration of its last `last` launches and its launch count, and
+    the sum of those means over the library's kernels."""
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        grid = "x".join(r.get(k, "1") for k in ("Grid_Size_X", "Grid_Size_Y"))
+        wg = r.get("Workgroup_Size_X", "")
+        key = (short_kernel_name(r["Kernel_Name"]), grid, wg)
+        acc.setdefault(key, []).append(
+            (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    ours = set(CE_KERNELS) | set(LOOKUP_GRAD_KERNELS) | {
+        "embed_kernel", "logits_stats_kernel", "dlogits_from_logits_kernel", "rows_max_kernel"}
+    rows = []
+    for (k, grid, wg), v in acc.items():
+        if k not in ours:
+            continue
+        v.sort()
+        tail = [d for _, d in v[-last:]]
+        rows.append((sum(tail) / len(tail), k, grid, wg, len(v)))
+    rows.sort(reverse=True)
+    lines = [f"# rocprofv3 kernel trace: {title}", "# command (from the repository root):",
+             f"#   {cmd}",
+             f"#   python3 bench.py --reduce-trace <kernel_trace csv> {name} '<title>' '<command>'",
+             f"kernel_source_hash: {kernel_source_hash()}", "",
+             f"## per-launch durations, mean of the last {last} launches of each kernel, microseconds"]
+    for us, k, grid, wg, n in rows:
+        lines.append(f"  {us:8.1f}  {k} [grid {grid} x {wg}]  (launches in run: {n})")
+    lines += ["", f"sum of the listed kernels (one launch each): {sum(r[0] for r in rows):.1f} us"]
+    with open(os.path.join(ROOT, "profiles", f"{name}.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 MFMA_PROFILE = os.path.join(ROOT, "profiles", "mfma_util_shard_8b.txt")
 MFMA_COUNTERS = "GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA"
 
@@ -441,7 +475,13 @@ def main():
     ap.add_argument("--reduce-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script into profiles/ and exit (no GPU needed)")
+    ap.add_argument("--reduce-trace", nargs=4, metavar=("TRACE_CSV", "NAME", "TITLE", "COMMAND"),
+                    help="summarise a rocprofv3 --kernel-trace CSV into profiles/NAME.txt and exit "
+                         "(no GPU needed)")
     args = ap.parse_args()
+    if args.reduce_trace:
+        reduce_trace(*args.reduce_trace)
+        return
     # the counter runs' commands, as recorded in the summaries: the output folder is the
     # one the given CSV files were written to (rocprofv3 -d <folder> -o run)
     run_args = "-o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline " \

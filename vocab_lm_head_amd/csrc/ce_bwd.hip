@@ -8,8 +8,8 @@
 // glossary "Tensor Parallelism"); the weight gradient is local.
 //
 // Steps (all on the caller's stream):
-//   1. X -> X^T and W_r -> W_r^T (bf16, rows zero-padded to a multiple of 64
-//      elements), so that all three GEMMs are K-contiguous on both operands;
+//   1. X -> X^T and W_r -> W_r^T in one launch (bf16, rows zero-padded to a multiple of
+//      64 elements), so that all three GEMMs are K-contiguous on both operands;
 //   2. recompute z^T = W_r X^T on MFMA; the epilogue forms
 //      dz = g (exp(z - lse) - onehot) in registers, stages the tile in LDS and
 //      writes it in bf16 twice, token-major dz [N, Vs64] and vocab-major dz^T [Vs, N64];
@@ -29,13 +29,25 @@ namespace {
 
 // out[c, r] = in[r, c] for r < rows, c < cols; out[c, r] = 0 for rows <= r < ld_out.
 // in: [rows, cols] row-major (cols multiple of 8); out: [cols, ld_out] (ld_out multiple of 8).
+struct TransposeJob {
+    const uint16_t *in;
+    int64_t rows;
+    uint16_t *out;
+    int64_t ld_out;
+};
+
+// Two transposes of the same column count in one launch: blockIdx.x below `split` tiles
+// job `a`, the rest job `b`; blockIdx.y walks the columns.
 constexpr int kTT = 64;
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__restrict__ in,
-                                                             int64_t rows, int64_t cols,
-                                                             uint16_t *__restrict__ out,
-                                                             int64_t ld_out) {
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(TransposeJob ja, TransposeJob jb,
+                                                             int64_t cols, unsigned split) {
     __shared__ uint16_t tile[kTT][kTT + 2];
-    const int64_t r0 = (int64_t)blockIdx.x * kTT;   // input rows  = output columns
+    const bool first = blockIdx.x < split;
+    const TransposeJob j = first ? ja : jb;
+    const uint16_t *__restrict__ in = j.in;
+    uint16_t *__restrict__ out = j.out;
+    const int64_t rows = j.rows, ld_out = j.ld_out;
+    const int64_t r0 = (int64_t)(first ? blockIdx.x : blockIdx.x - split) * kTT;   // input rows  = output columns
     const int64_t c0 = (int64_t)blockIdx.y * kTT;   // input cols  = output rows
     const int t = threadIdx.x;
     {
@@ -70,13 +82,6 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t *__r
             *(u32x4 *)(out + grow * ld_out + gcol) = v;
         }
     }
-}
-
-hipError_t transpose_bf16(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out,
-                          int64_t ld_out, hipStream_t stream) {
-    dim3 grid((unsigned)ceil_div(ld_out, kTT), (unsigned)ceil_div(cols, kTT));
-    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, stream, in, rows, cols, out, ld_out);
-    return hipGetLastError();
 }
 
 // dz = g (softmax - onehot) from the recomputed z^T tile; rows = vocab, cols = tokens.
@@ -284,10 +289,12 @@ hipError_t launch_bwd_transposes(const uint16_t *x, const uint16_t *w, int64_t n
                                  int64_t vs, void *ws, hipStream_t stream) {
     const BwdWorkspace b = bwd_workspace(n, h, vs);
     char *base = (char *)ws;
-    hipError_t e;
-    if ((e = transpose_bf16(x, n, h, (uint16_t *)(base + b.off_xt), b.n_ld, stream)) != hipSuccess)
-        return e;
-    return transpose_bf16(w, vs, h, (uint16_t *)(base + b.off_wt), b.vs_ld, stream);
+    const TransposeJob jx{x, n, (uint16_t *)(base + b.off_xt), b.n_ld};
+    const TransposeJob jw{w, vs, (uint16_t *)(base + b.off_wt), b.vs_ld};
+    const unsigned split = (unsigned)ceil_div(b.n_ld, kTT);
+    dim3 grid(split + (unsigned)ceil_div(b.vs_ld, kTT), (unsigned)ceil_div(h, kTT));
+    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, stream, jx, jw, h, split);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_grad_gemms(int64_t n, int64_t h, int64_t vs, float *dx, float *dw, void *ws,
