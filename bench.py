@@ -238,7 +238,7 @@ def reduce_pmc(fetch_csv, write_csv, cmd_fetch, cmd_write):
     print("\n".join(lines))
 
 
-def reduce_trace(path, name, title, cmd, last=5):
+def reduce_trace(path, name, title, cmd, last=5, bench_log=None):
     """Summarise a rocprofv3 --kernel-trace CSV into profiles/<name>.txt: per kernel (short
     name and grid), the mean duration of its last `last` launches and its launch count, and
     the sum of those means over the library's kernels."""
@@ -267,6 +267,44 @@ def reduce_trace(path, name, title, cmd, last=5):
     for us, k, grid, wg, n in rows:
         lines.append(f"  {us:8.1f}  {k} [grid {grid} x {wg}]  (launches in run: {n})")
     lines += ["", f"sum of the listed kernels (one launch each): {sum(r[0] for r in rows):.1f} us"]
+    # the CE sequence of each traced step: from the forward GEMM that follows a lookup to the
+    # last kernel before the next lookup (the step's own order: lookup, fwd, combine, bwd)
+    seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                  short_kernel_name(r["Kernel_Name"])) for r in csv.DictReader(open(path)))
+    spans = []
+    for i, (_, _, k) in enumerate(seq):
+        if k != "embed_kernel" or i + 1 >= len(seq) or seq[i + 1][2] != "CeStatsEpilogue":
+            continue
+        # the sequence ends with the backward's second gradient GEMM after its recompute
+        j, grads = i + 1, -1
+        while j + 1 < len(seq) and seq[j + 1][2] in CE_KERNELS and grads < 2:
+            j += 1
+            if seq[j][2] == "DlogitsEpilogue":
+                grads = 0
+            elif grads >= 0 and seq[j][2] in ("StoreTransposedEpilogue", "gemm_nt_splitk_store_kernel"):
+                grads += 1
+        if grads == 2:
+            spans.append((seq[j][1] - seq[i + 1][0]) / 1e3)
+    if spans:
+        tail = spans[-last:]
+        lines.append(f"CE sequence (forward GEMM start to dW GEMM end), last {len(tail)} steps: "
+                     f"{sum(tail) / len(tail):.1f} us")
+    if bench_log:   # the bench's own HIP-event figures from the same run
+        for line in open(bench_log):
+            if line.startswith("{") and '"roofline"' in line:
+                d = json.loads(line)
+                lines.append(f"bench.py HIP events in the same (profiled) run: CE sequence "
+                             f"{d['roofline']['avg_launch_ms'] * 1e3:.1f} us, step "
+                             f"{d['ms_per_step'] * 1e3:.1f} us")
+    stats = os.path.join(os.path.dirname(path), os.path.basename(path).replace("kernel_trace", "kernel_stats"))
+    if os.path.exists(stats) and stats != path:
+        lines += ["", "## rocprofv3 --stats (every launch of the run, warm-up and untimed calls included)",
+                  "calls  avg_us  min_us  max_us  kernel"]
+        for r in csv.DictReader(open(stats)):
+            k = short_kernel_name(r["Name"])
+            if k in ours:
+                lines.append(f"{int(r['Calls']):5d} {float(r['AverageNs']) / 1e3:7.1f} "
+                             f"{float(r['MinNs']) / 1e3:7.1f} {float(r['MaxNs']) / 1e3:7.1f}  {k}")
     with open(os.path.join(ROOT, "profiles", f"{name}.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -478,9 +516,10 @@ def main():
     ap.add_argument("--reduce-trace", nargs=4, metavar=("TRACE_CSV", "NAME", "TITLE", "COMMAND"),
                     help="summarise a rocprofv3 --kernel-trace CSV into profiles/NAME.txt and exit "
                          "(no GPU needed)")
+    ap.add_argument("--bench-log", help="with --reduce-trace: the bench output of the traced run")
     args = ap.parse_args()
     if args.reduce_trace:
-        reduce_trace(*args.reduce_trace)
+        reduce_trace(*args.reduce_trace, bench_log=args.bench_log)
         return
     # the counter runs' commands, as recorded in the summaries: the output folder is the
     # one the given CSV files were written to (rocprofv3 -d <folder> -o run)
