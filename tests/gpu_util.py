@@ -105,21 +105,6 @@ def run_ce_path(vp, x_d, w_shards_d, starts, ends, tgt_d, grad_scale, bwd_shards
     return {"loss": loss, "lse": lse, "mean": mean, "m": m, "s": s, "zy": zy, "grads": grads}
 
 
-def sampled_grads(out, t, x, w_shard, y, lse_ref, start, g, rng, k_rows=24, k_cols=24):
-    """Compare sampled rows of dX_t and dW_t with the oracle evaluated on those rows."""
-    n, vs = x.shape[0], w_shard.shape[0]
-    k_rows, k_cols = min(k_rows, n), min(k_cols, vs)
-    rows = np.unique(np.concatenate([rng.choice(n, k_rows, replace=False), [0, n - 1]]))
-    dzr = oracle.dz_rows(x[rows], w_shard, y[rows], lse_ref[rows], start, g)
-    assert_grad_close(host(out["grads"][t][0][rows]), dzr @ w_shard, f"dX_{t} ({rows.size} rows)")
-    # vocabulary rows: random ones, both ends, and rows that are targets
-    own = y[(y >= start) & (y < start + vs)] - start
-    cols = np.unique(np.concatenate([rng.choice(vs, k_cols, replace=False), [0, vs - 1],
-                                     own[:8]])).astype(np.int64)
-    dzc = oracle.dz_cols(x, w_shard[cols], cols + start, y, lse_ref, g)
-    assert_grad_close(host(out["grads"][t][1][cols]), dzc.T @ x, f"dW_{t} ({cols.size} rows)")
-
-
 def _rel_max_device(got_d, ref, rows_per_piece=2048):
     """max|got - ref| / max|ref| over whole tensors, with ``got_d`` (a GPU tensor) brought
     to the host a slab of rows at a time (a full-size gradient in fp64 would double host

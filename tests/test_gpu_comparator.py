@@ -12,7 +12,7 @@ import pytest
 import oracle
 import vp_inputs
 from gpu_util import (assert_grad_close, assert_loss_close, assert_stats_close, dev_bf16, dev_i64,
-                      host, log, sampled_grads)
+                      full_grads, host, log)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,6 +106,7 @@ def test_ragged_shards_and_rows(vp):
     _full_check(vp, xb, wb, y, T, True, "ragged")
 
 
+@pytest.mark.timeout(900)
 def test_shard_8b_against_golden(vp):
     """The 8B-class shard 0 ([16032, 4096], N = 8192), statistics in one read: every token's
     loss and lse against the oracle golden (shards 1..7's statistics from their fused
@@ -145,7 +146,7 @@ def test_shard_8b_against_golden(vp):
                        - oracle.logits(x[rows], w)).max())
     log(f"  stored logits (24 rows): max abs err {err:.2e}")
     assert err <= 2e-3
-    sampled_grads({"grads": {0: grads}}, 0, x, w, y, gold["lse"], lo, g, r)
+    full_grads({"grads": {0: grads}}, 0, x, w, y, gold["lse"], lo, g)
 
 
 def _sweep_cases():

@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import vp_inputs
-from gpu_util import (U, dev_bf16, dev_i64, embed_bwd_assert_rows, embed_bwd_full_check,
+from gpu_util import (U, dev_bf16, dev_i64, embed_bwd_full_check,
                       embed_bwd_run, host, log)
 
 pytestmark = pytest.mark.gpu
@@ -109,38 +109,28 @@ def test_edges(vp, case):
     embed_bwd_full_check(vp, ids, dout, lo, hi, dw0, case)
 
 
+@pytest.mark.timeout(900)
 def test_embedding_heavy_backward(vp):
-    """65536 Zipf(1.0) ids on shard 0 ([64000, 4096] of V=256000, T=4): the 8 most
-    repeated rows, 24 other owned rows, 8 rows no id names and both shard ends, plus
-    every column's total over the shard against the owned tokens' total."""
+    """65536 Zipf(1.0) ids on shard 0 ([64000, 4096] of V=256000, T=4), added into a random
+    prefilled gradient (the tied shard's LM-head gradient): every row of the shard against the
+    oracle's scatter-add within the summation bound (rows no id names unchanged bit for bit),
+    plus every column's total over the shard against the owned tokens' total."""
     import torch
     inp = vp_inputs.make_inputs("embedding_heavy", with_weight=False)
     wl = inp.wl
     lo, hi = vp.vp_shard_range(wl.embed_V, wl.embed_T, 0)
     ids = inp.ids
     dout = vp_inputs.make_embed_output_grad("embedding_heavy")
-    dw = torch.zeros((hi - lo, wl.embed_H), dtype=torch.float32, device="cuda")
-    vp.vp_embed_bwd(dev_i64(ids), dev_bf16(dout), lo, hi, dw)
-    torch.cuda.synchronize()
     own = (ids >= lo) & (ids < hi)
-    local = ids[own] - lo
-    rows, counts = np.unique(local, return_counts=True)
-    r = np.random.default_rng(8)
-    top = rows[np.argsort(-counts, kind="stable")[:8]]
-    others = r.choice(np.setdiff1d(rows, top), 24, replace=False)
-    untouched = r.choice(np.setdiff1d(np.arange(hi - lo), rows), 8, replace=False)
-    pick = np.unique(np.concatenate([top, others, untouched, [0, hi - lo - 1]]))
-    got = host(dw[torch.from_numpy(pick).cuda()])
+    rows, counts = np.unique(ids[own] - lo, return_counts=True)
     log(f"  {own.sum()} owned ids, {rows.size} distinct rows, most repeated row x{counts.max()}")
-    # a row depends only on its own tokens: hand the oracle just those
-    sub = own & np.isin(ids - lo, pick)
-    dw0 = np.zeros((hi - lo, wl.embed_H), np.float32)
-    embed_bwd_assert_rows(got, dw0, ids[sub], vp_inputs.bf16_bits_to_f64(dout[sub]), lo, pick,
-                 "embedding-heavy sampled rows")
+    dw0 = (np.random.default_rng(8).standard_normal((hi - lo, wl.embed_H), dtype=np.float32)
+           * np.float32(1e-3))
+    got = embed_bwd_full_check(vp, ids, dout, lo, hi, dw0, "embedding-heavy, every row")
     dout_f = vp_inputs.bf16_bits_to_f64(dout[own])
-    col_gpu = dw.double().sum(dim=0).cpu().numpy()
+    col_gpu = (got - dw0.astype(np.float64)).sum(axis=0)
     col_ref = dout_f.sum(axis=0)
-    mag = np.abs(dout_f).sum(axis=0)
+    mag = np.abs(dout_f).sum(axis=0) + np.abs(dw0).astype(np.float64).sum(axis=0)
     err = np.abs(col_gpu - col_ref)
     log(f"  column totals: max abs err {err.max():.3e}")
-    assert np.all(err <= (own.sum() + 2) * U * mag + 1e-9)
+    assert np.all(err <= (own.sum() + 2) * U * mag * 2 + 1e-9)
