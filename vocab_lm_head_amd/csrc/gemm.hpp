@@ -16,11 +16,20 @@
 // LDS rows are 64 bf16 = 128 B = eight 16-byte chunks; chunk c of row r is
 // stored at chunk c ^ (r & 7) so that the 16-lane groups of a fragment read
 // (16 consecutive rows, one chunk) hit distinct banks.
-// Global -> LDS goes through buffer loads straight into LDS (buffer_load ... lds):
-// the loads of K step k+2 are issued in the second half of step k, into the stage
-// step k has just finished with.  Operand fragments are double-buffered in
-// registers so that the LDS reads of one half K step overlap the MFMAs of the
-// other; one barrier per K step.
+// Global -> LDS goes through buffer loads straight into LDS (buffer_load ... lds).
+//
+// Ping-pong schedule.  The CU places wave w and wave w + 4 of a workgroup on the same
+// SIMD (measured with the HW_ID register), so waves 0-3 (group 0) and 4-7 (group 1)
+// each hold one wave per SIMD.  The groups run half a K step apart, separated by
+// workgroup barriers: in each interval one group reads a whole K step's fragments
+// from LDS and issues its global loads while the other runs that step's 64 MFMAs, so
+// the SIMD's matrix core is fed by one wave while the other waits on memory.  Group g
+// computes M half g; group 0 loads the A tiles, group 1 the B tiles.  With K step k in
+// LDS stage k % 2, interval 2k holds group 0's reads of step k and its loads of A(k+1)
+// (into the other stage, which group 1 finished reading in interval 2k - 1); interval
+// 2k + 1 holds group 1's reads of step k, then, once they are complete, its loads of
+// B(k+2) into the same stage (group 0 read it in interval 2k).  Each load has landed one
+// interval before the first read of it.
 //
 // Rows past M / N read as zeros (outside the buffer resource; the epilogue
 // masks them); K chunks past K are zero-filled, so K need only be a multiple
@@ -45,8 +54,6 @@ constexpr int kWM = kBM / kWavesM;          // wave tile rows
 constexpr int kWN = kBN / kWavesN;          // wave tile cols
 constexpr int kTM = kWM / 16;               // MFMA tiles per wave along M
 constexpr int kTN = kWN / 16;               // MFMA tiles per wave along N
-constexpr int kGA = kBM / 8 / kWaves;       // 8-row groups of A each wave loads per K step
-constexpr int kGB = kBN / 8 / kWaves;       // ... and of B
 constexpr int kGroupM = 8;         // tiles per raster group along M
 // s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8])
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -109,11 +116,30 @@ __device__ __forceinline__ void store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint3
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolicy);
 }
 
-// One K step of operand fragments held by a wave: 8 A rows-blocks and 8 B col-blocks.
+// One K step of operand fragments held by a wave: for each 32-wide half of the step,
+// kTM A row blocks and kTN B column blocks.
 struct Frags {
-    bf16x8 a[kTM];
-    bf16x8 b[kTN];
+    bf16x8 a[2][kTM];
+    bf16x8 b[2][kTN];
 };
+
+static_assert(kWaves == 8 && kWavesM == 2 && kBM == kBN && kBM / kWavesN == 64,
+              "ping-pong layout: two groups of four waves, one 64-row load slab per wave");
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
+constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkmcnt0 = 0xC07F;
+
+// A workgroup barrier that orders nothing by itself: the memory waits around it are
+// explicit, so that loads may stay in flight across it.  The empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
 
 // two LDS stages of one [256 x 64] A tile and one [256 x 64] B tile each (2 x 64 KiB)
 constexpr int kStage = (kBM + kBN) * kBK;
@@ -129,59 +155,55 @@ __device__ __forceinline__ void gemm_nt_tile(const Operand &A, const Operand &B,
     const int m0 = tm * kBM, n0 = tn * kBN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
-    const int wm = wave % kWavesM, wn = wave / kWavesM;
+    const int grp = wave >> 2, slab = wave & 3;   // group; the wave's place in it (its SIMD)
+    const int wm = grp, wn = slab;
 
     // Global -> LDS map (buffer loads straight into LDS, 16 bytes per lane).  One wave
     // instruction fills 8 rows x 128 B = 1 KiB of LDS in lane order: lane L lands on
     // row L/8, physical chunk L%8, so it fetches the logical chunk (L%8) ^ (row & 7).
-    // Wave w fills 8-row groups w*kGA .. (w+1)*kGA-1 of A and w*kGB .. of B.
+    // Group 0 loads A and group 1 loads B; wave `slab` of a group loads rows
+    // 64 slab .. 64 slab + 63 of its operand's tile, eight instructions per K step.
     // The buffer resource starts at the tile's first row and ends at the tensor's
     // end, so rows past M (or N) fall outside it and read as zeros.
+    const Operand &L = grp ? B : A;
+    const int r0 = grp ? n0 : m0;
     const int lrow = lane >> 3;
     const int lchunk = (lane & 7) ^ lrow;
-    const char *a_panel = (const char *)(A.p + (int64_t)m0 * A.ld);
-    const char *b_panel = (const char *)(B.p + (int64_t)n0 * B.ld);
+    const char *panel = (const char *)(L.p + (int64_t)r0 * L.ld);
     // bytes from the panel start to the end of the last row (past it: zeros)
-    const uint32_t a_bytes = resource_bytes((int64_t)(A.rows - m0) * A.ld * 2);
-    const uint32_t b_bytes = resource_bytes((int64_t)(B.rows - n0) * B.ld * 2);
-    const uint32_t a_row8 = (uint32_t)(8 * A.ld * 2), b_row8 = (uint32_t)(8 * B.ld * 2);
-    const uint32_t a_off0 = (uint32_t)(((wave * kGA * 8 + lrow) * A.ld + lchunk * 8) * 2);
-    const uint32_t b_off0 = (uint32_t)(((wave * kGB * 8 + lrow) * B.ld + lchunk * 8) * 2);
-    const int grp_a = wave * kGA * 8 * kBK;   // LDS element offsets of this wave's first groups
-    const int grp_b = kBM * kBK + wave * kGB * 8 * kBK;
+    const uint32_t bytes = resource_bytes((int64_t)(L.rows - r0) * L.ld * 2);
+    const uint32_t row8 = (uint32_t)(8 * L.ld * 2);
+    const uint32_t off0 = (uint32_t)(((64 * slab + lrow) * L.ld + lchunk * 8) * 2);
+    const int dst0 = (grp ? kBM * kBK : 0) + 64 * slab * kBK;   // LDS element offset in a stage
 
     // Branch-free: a chunk at or past K (the last partial K step, or a step past the
     // end) gets an offset outside the resource, which reads as zeros.
-    auto load_tile = [&](uint16_t *buf, int k0) {
-        const __amdgpu_buffer_rsrc_t ra =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(a_panel + 2 * k0), (short)0, a_bytes, kBufferFlags);
-        const __amdgpu_buffer_rsrc_t rb =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(b_panel + 2 * k0), (short)0, b_bytes, kBufferFlags);
-        const bool ok = k0 + lchunk * 8 < K;
-        const uint32_t oa = ok ? a_off0 : kOutOfRange;
-        const uint32_t ob = ok ? b_off0 : kOutOfRange;
+    auto load_slab = [&](int st, int k0) {
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(panel + 2 * k0), (short)0, bytes, kBufferFlags);
+        const uint32_t o = k0 + lchunk * 8 < K ? off0 : kOutOfRange;
+        uint16_t *dst = smem + st * kStage + dst0;
 #pragma unroll
-        for (int i = 0; i < kGA; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(buf + grp_a + i * 8 * kBK), 16,
-                                                     oa + i * a_row8, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < kGB; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(buf + grp_b + i * 8 * kBK), 16,
-                                                     ob + i * b_row8, 0, 0, 0);
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + i * 8 * kBK), 16,
+                                                     o + i * row8, 0, 0, 0);
     };
 
     // fragment map: lane reads row (lane & 15) of each 16-row tile, logical chunk kk*4 + lane/16
     const int fr = lane & 15;
     const int a_off = (wm * kWM + fr) * kBK;
     const int b_off = kBM * kBK + (wn * kWN + fr) * kBK;
-    const int ch0 = ((0 + (lane >> 4)) ^ (fr & 7)) * 8;
-    const int ch1 = ((4 + (lane >> 4)) ^ (fr & 7)) * 8;
+    const int ch[2] = {((0 + (lane >> 4)) ^ (fr & 7)) * 8, ((4 + (lane >> 4)) ^ (fr & 7)) * 8};
 
-    auto read_frags = [&](const uint16_t *buf, int ch, Frags &f) {
+    auto read_step = [&](int st, Frags &f) {
+        const uint16_t *buf = smem + st * kStage;
 #pragma unroll
-        for (int i = 0; i < kTM; ++i) f.a[i] = *(const bf16x8 *)&buf[a_off + i * 16 * kBK + ch];
+        for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) f.b[j] = *(const bf16x8 *)&buf[b_off + j * 16 * kBK + ch];
+            for (int i = 0; i < kTM; ++i) f.a[kk][i] = *(const bf16x8 *)&buf[a_off + i * 16 * kBK + ch[kk]];
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) f.b[kk][j] = *(const bf16x8 *)&buf[b_off + j * 16 * kBK + ch[kk]];
+        }
     };
 
     Acc acc;
@@ -190,67 +212,53 @@ __device__ __forceinline__ void gemm_nt_tile(const Operand &A, const Operand &B,
 #pragma unroll
         for (int j = 0; j < kTN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto mma = [&](const Frags &f, int i0, int i1) {
+    auto mma_step = [&](const Frags &f) {
 #pragma unroll
-        for (int i = i0; i < i1; ++i)
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int j = 0; j < kTN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0);
     };
 
     const int KT = (int)ceil_div(K, kBK);
-    constexpr int kReads = kTM + kTN;    // LDS fragment reads per half K step
-    constexpr int kMfmas = kTM * kTN;    // MFMAs per half K step
-    static_assert(kMfmas >= 2 * kReads && kMfmas >= kGA + kGB + kReads, "schedule shape");
-    Frags f0, f1;
-
-    load_tile(smem, 0);
-    load_tile(smem + kStage, kBK);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    read_frags(smem, ch0, f0);
-
-    // K step kt works on the tile in stage kt & 1; the next tile is in the other stage.
-    // F0 (K 0..31 of the step) is already in registers when the step starts.  The
-    // sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read, 0x020 global/buffer load.
-    for (int kt = 0; kt < KT; ++kt) {
-        uint16_t *cur = smem + (kt & 1) * kStage;
-        uint16_t *nxt = smem + ((kt + 1) & 1) * kStage;
-        // phase 1: F0's MFMAs, with F1's LDS reads spread over the first of them
-        read_frags(cur, ch1, f1);
-        mma(f0, 0, kTM);
-#pragma unroll
-        for (int q = 0; q < kReads; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - 2 * kReads, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        // every wave has its F1 (nobody reads `cur` any more) and tile kt+1 has landed;
-        // no branch: past the last step the loads read zeros and F0 is unused
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        // phase 2: F1's MFMAs, with tile kt+2's loads and the next F0's reads
-        load_tile(cur, (kt + 2) * kBK);
-        read_frags(nxt, ch0, f0);
-        mma(f1, 0, kTM);
-#pragma unroll
-        for (int q = 0; q < kGA + kGB; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < kReads; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kGA - kGB - kReads, 0);
-        __builtin_amdgcn_sched_barrier(0);
+    // Prologue: A(0) from group 0, B(0) and B(1) from group 1.  Group 1 then sits out
+    // interval 0 and group 0 the last interval, so every wave passes 2 KT + 3 barriers
+    // (this one, the two per K step, the extra one and the one before the epilogue).
+    load_slab(0, 0);
+    if (grp == 0) {
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    } else {
+        load_slab(1, kBK);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));   // B(0) has landed; B(1) may be in flight
     }
+    bare_barrier();
+    if (grp == 1) bare_barrier();
+    Frags f;
+    for (int k = 0; k < KT; ++k) {
+        const int st = k & 1;
+        // memory interval: this K step's fragments, then the group's loads
+        read_step(st, f);
+        if (grp == 0) {
+            load_slab(st ^ 1, (k + 1) * kBK);              // A(k+1)
+        } else {
+            __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);     // this wave's reads of stage st are done
+            load_slab(st, (k + 2) * kBK);                  // B(k+2)
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));     // B(k+1) has landed
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+        bare_barrier();
+        // compute interval: the step's 64 MFMAs
+        mma_step(f);
+        __builtin_amdgcn_sched_barrier(0);
+        if (grp == 0) __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));   // A(k+1) has landed
+        bare_barrier();
+    }
+    if (grp == 0) bare_barrier();
 
-    // The last steps' loads (zeros) may still be landing and other waves may still be
-    // reading: drain both before an epilogue reuses the LDS.
+    // Past the last K step the loads (zeros) may still be landing: drain them before an
+    // epilogue reuses the LDS.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
