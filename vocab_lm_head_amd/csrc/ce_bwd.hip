@@ -19,6 +19,7 @@
 // dW would need fp32 atomics on [tile, H] slabs for every tile, far below the
 // MFMA roofline at H = 4096.
 #include <algorithm>
+#include <type_traits>
 
 #include "gemm.hpp"
 #include "launch.hpp"
@@ -124,26 +125,41 @@ struct DlogitsEpilogue {
             ls[j] = lse[nc];
         }
         __builtin_amdgcn_sched_barrier(0);
+        // Only a wave tile that crosses the shard's last row or the last token needs the
+        // padding mask: the loop is instantiated twice, picked by a wave-uniform branch.
+        auto body = [&](auto edge_tag) {
+            constexpr bool kEdge = decltype(edge_tag)::value;
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) {
-            const int n = nbase + 16 * j + (lane & 15);
-            const bool ncol = n < N;
-            const float g = (tg[j] == ignore_index) ? 0.f : grad_scale;
-            const float lsel = ls[j] * kLog2e;
-            const int64_t trow = tg[j] - start;
+            for (int j = 0; j < kTN; ++j) {
+                const int n = nbase + 16 * j + (lane & 15);
+                const bool ncol = n < N;
+                const float g = (tg[j] == ignore_index) ? 0.f : grad_scale;
+                const float lsel = ls[j] * kLog2e;
+                // the target's row relative to this lane's first row (element 16 i + r), or -1;
+                // the asm keeps the range test out of the per-element comparisons
+                const int64_t rel = tg[j] - start - mbase - rsub;
+                int trel = (rel >= 0 && rel < kWM) ? (int)rel : -1;
+                asm volatile("" : "+v"(trel));
 #pragma unroll
-            for (int i = 0; i < kTM; ++i) {
-                const int row0 = mbase + 16 * i + rsub;   // vocabulary row of r = 0
-                float d[4];
+                for (int i = 0; i < kTM; ++i) {
+                    const int row0 = mbase + 16 * i + rsub;   // vocabulary row of r = 0
+                    f32x4 d;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(fmaf(acc[i][j][r], kLog2e, -lsel));
-                    const float v = g * (p - ((row0 + r) == trow ? 1.f : 0.f));
-                    d[r] = (ncol && (row0 + r) < M) ? v : 0.f;   // padding stays exactly 0
+                    for (int r = 0; r < 4; ++r) {
+                        const float p = fast_exp2(fmaf(acc[i][j][r], kLog2e, -lsel));
+                        const float gs = trel == 16 * i + r ? g : 0.f;   // g at the target
+                        d[r] = fmaf(g, p, -gs);
+                        if (kEdge) d[r] = (ncol && row0 + r < M) ? d[r] : 0.f;   // padding stays exactly 0
+                    }
+                    *(u32x2 *)(lds + dz_swz(n - n0, row0 - m0)) =
+                        __builtin_bit_cast(u32x2, __builtin_convertvector(d, bf16x4));
                 }
-                *(u32x2 *)(lds + dz_swz(n - n0, row0 - m0)) = pack_bf16x4(d[0], d[1], d[2], d[3]);
             }
-        }
+        };
+        if (mbase + kWM > M || nbase + kWN > N)
+            body(std::true_type{});
+        else
+            body(std::false_type{});
         __syncthreads();
         const int t = threadIdx.x;
         // Both passes read all of their LDS chunks first, then issue their stores; rows

@@ -77,22 +77,31 @@ struct CeStatsEpilogue {
         float sum[kTN], zy[kTN];
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
-            // target row relative to this lane's first row; matches 16 i + r for at most
-            // one (i, r), and never when the target lies outside the shard
+            // The target's row relative to this lane's first row is 16 it + rt, with rt < 4,
+            // for at most one lane of the column, and never when the target lies outside the
+            // shard: pick MFMA tile it, then its component rt.  (The asm keeps the compiler
+            // from splitting the range test into every comparison.)
             const int64_t local = tg[j] - start;
-            const int tr = (local >= 0 && local < M) ? (int)(local - mbase) - rsub : -1;
+            int tr = (local >= 0 && local < M) ? (int)(local - mbase) - rsub : -1;
+            asm volatile("" : "+v"(tr));
+            const int it = tr >> 4, rt = tr & 15;
+            f32x4 t4 = acc[0][j];
+#pragma unroll
+            for (int i = 1; i < kTM; ++i) t4 = (it == i) ? acc[i][j] : t4;
+            const float z = rt == 0 ? t4[0] : rt == 1 ? t4[1] : rt == 2 ? t4[2] : t4[3];
+            zy[j] = (tr >= 0 && tr < kWM && rt < 4) ? z : 0.f;
+            // the sum of exponentials about the column maximum, in two interleaved partial
+            // sums (two independent dependency chains)
             const float mxl = mx[j] * kLog2e;
-            float sj = 0.f, zj = 0.f;
+            float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-            for (int i = 0; i < kTM; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = acc[i][j][r];
-                    sj += fast_exp2(fmaf(v, kLog2e, -mxl));
-                    zj = (tr == 16 * i + r) ? v : zj;
-                }
-            sum[j] = sj;
-            zy[j] = zj;
+            for (int i = 0; i < kTM; ++i) {
+                s0 += fast_exp2(fmaf(acc[i][j][0], kLog2e, -mxl));
+                s1 += fast_exp2(fmaf(acc[i][j][1], kLog2e, -mxl));
+                s0 += fast_exp2(fmaf(acc[i][j][2], kLog2e, -mxl));
+                s1 += fast_exp2(fmaf(acc[i][j][3], kLog2e, -mxl));
+            }
+            sum[j] = s0 + s1;
         }
 #pragma unroll
         for (int j = 0; j < kTN; ++j) {
