@@ -134,7 +134,7 @@ struct CeStatsEpilogue {
 // written at row blockIdx.y of the outputs (rows out_stride apart).  The input and the
 // output rows share one layout, [3][rows][n] (max, sum-exp, target logit), so the
 // same kernel merges the per-split results of a first pass.
-constexpr int kMergeTok = 32, kMergeGrp = 8, kMergeBatch = 4;
+constexpr int kMergeTok = 32, kMergeGrp = 8, kMergeBatch = 16;
 __global__ __launch_bounds__(kMergeTok * kMergeGrp) void merge_slices_kernel(
     const float *__restrict__ part, int64_t slices, int64_t n, int64_t chunk,
     float *__restrict__ m_out, float *__restrict__ s_out, float *__restrict__ zy_out,
