@@ -28,8 +28,8 @@
 // LDS stage k % 2, interval 2k holds group 0's reads of step k and its loads of A(k+1)
 // (into the other stage, which group 1 finished reading in interval 2k - 1); interval
 // 2k + 1 holds group 1's reads of step k, then, once they are complete, its loads of
-// B(k+2) into the same stage (group 0 read it in interval 2k).  Each load has landed one
-// interval before the first read of it.
+// B(k+2) into the same stage (group 0 read it in interval 2k).  Each load has landed
+// before the interval of its first read begins.
 //
 // Rows past M / N read as zeros (outside the buffer resource; the epilogue
 // masks them); K chunks past K are zero-filled, so K need only be a multiple
@@ -125,6 +125,8 @@ struct Frags {
 
 static_assert(kWaves == 8 && kWavesM == 2 && kBM == kBN && kBM / kWavesN == 64,
               "ping-pong layout: two groups of four waves, one 64-row load slab per wave");
+// load instructions one wave issues per K step: its 64-row slab, 8 rows per instruction
+constexpr int kSlabLoads = kBM / kWavesN / 8;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -184,7 +186,7 @@ __device__ __forceinline__ void gemm_nt_tile(const Operand &A, const Operand &B,
         const uint32_t o = k0 + lchunk * 8 < K ? off0 : kOutOfRange;
         uint16_t *dst = smem + st * kStage + dst0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < kSlabLoads; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + i * 8 * kBK), 16,
                                                      o + i * row8, 0, 0, 0);
     };
@@ -231,7 +233,7 @@ __device__ __forceinline__ void gemm_nt_tile(const Operand &A, const Operand &B,
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     } else {
         load_slab(1, kBK);
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));   // B(0) has landed; B(1) may be in flight
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(kSlabLoads));   // B(0) has landed; B(1) may be in flight
     }
     bare_barrier();
     if (grp == 1) bare_barrier();
@@ -245,7 +247,7 @@ __device__ __forceinline__ void gemm_nt_tile(const Operand &A, const Operand &B,
         } else {
             __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);     // this wave's reads of stage st are done
             load_slab(st, (k + 2) * kBK);                  // B(k+2)
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));     // B(k+1) has landed
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(kSlabLoads));   // B(k+1) has landed
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
         bare_barrier();
