@@ -218,44 +218,66 @@ __global__ void fill_zero_kernel(float *p, int64_t count) {
         p[i] = 0.f;
 }
 
-// Split-K form of the transposed store: the grid holds `splits` copies of the tile grid,
-// and copy s computes every tile over the K columns [s chunk, min((s + 1) chunk, K)) of
-// both operands (chunk a multiple of kBK, so the shifted rows stay 128-byte aligned) and
-// stores its partial at epi.out + s out_stride.  A reduction then sums the partials in
-// split order.  For outputs with too few tiles to fill the chip.
-__global__ __launch_bounds__(kThreads, 1) void gemm_nt_splitk_store_kernel(
-    Operand A, Operand B, int K, int chunk, int tiles_m, int tiles_n, StoreTransposedEpilogue epi,
-    int64_t out_stride) {
+// Split-K form of the transposed store, for outputs with too few tiles to fill the chip.
+// A job's grid holds `splits` copies of its tile grid; copy s computes every tile over the
+// K columns [s chunk, min((s + 1) chunk, K)) of both operands (chunk a multiple of kBK, so
+// the shifted rows stay 128-byte aligned) and stores its partial at epi.out + s out_stride.
+// A reduction then sums the partials in split order.  One launch runs up to two jobs:
+// workgroups [0, j0.blocks) take the first, the rest the second.
+struct SplitJob {
+    Operand A, B;
+    int K, chunk;
+    GemmGrid g;
+    StoreTransposedEpilogue epi;
+    int64_t out_stride;
+    int blocks;   // g.blocks() x splits
+};
+__global__ __launch_bounds__(kThreads, 1) void gemm_nt_splitk_store_kernel(SplitJob j0,
+                                                                           SplitJob j1) {
     __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * kStage];
-    const int tiles = tiles_m * tiles_n;
-    const int split = blockIdx.x / tiles;
-    const int k0 = split * chunk;
-    Operand a = A, b = B;
+    const bool first = (int)blockIdx.x < j0.blocks;
+    const SplitJob &j = first ? j0 : j1;
+    const int bid = first ? (int)blockIdx.x : (int)blockIdx.x - j0.blocks;
+    const int tiles = j.g.tiles_m * j.g.tiles_n;
+    const int split = bid / tiles;
+    const int k0 = split * j.chunk;
+    Operand a = j.A, b = j.B;
     a.p += k0;
     b.p += k0;
-    epi.out += split * out_stride;
-    gemm_nt_tile(a, b, min(chunk, K - k0), tiles_m, tiles_n, epi, blockIdx.x - split * tiles, smem);
+    StoreTransposedEpilogue epi = j.epi;
+    epi.out += split * j.out_stride;
+    gemm_nt_tile(a, b, min(j.chunk, j.K - k0), j.g.tiles_m, j.g.tiles_n, epi, bid - split * tiles,
+                 smem);
 }
 
-// out[i] = sum over s of part[s stride + i] for i < count, in split order (fp32).  count
-// and stride are multiples of 4 and the buffers 16-byte aligned.
+// out[i] = sum over s of part[s stride + i] for i < count, in split order (fp32), for up to
+// two jobs (threads past the first job's count / 4 take the second).  count and stride are
+// multiples of 4 and the buffers 16-byte aligned.
 constexpr int kMaxSplits = 16;
-__global__ __launch_bounds__(256) void sum_splits_kernel(const float *__restrict__ part, int splits,
-                                                         int64_t count, int64_t stride,
-                                                         float *__restrict__ out) {
-    const f32x4 *p = (const f32x4 *)part;
-    const int64_t n4 = count / 4, s4 = stride / 4;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-         i += (int64_t)gridDim.x * blockDim.x) {
+struct SumJob {
+    const float *part;
+    int splits;
+    int64_t count, stride;
+    float *out;
+};
+__global__ __launch_bounds__(256) void sum_splits_kernel(SumJob j0, SumJob j1) {
+    const int64_t n0 = j0.count / 4, n4 = n0 + j1.count / 4;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n4;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const bool first = t < n0;
+        const SumJob &j = first ? j0 : j1;
+        const int64_t i = first ? t : t - n0;
+        const f32x4 *p = (const f32x4 *)j.part;
+        const int64_t s4 = j.stride / 4;
         f32x4 v[kMaxSplits];
 #pragma unroll
         for (int s = 0; s < kMaxSplits; ++s)
-            if (s < splits) v[s] = p[s * s4 + i];
+            if (s < j.splits) v[s] = p[s * s4 + i];
         f32x4 acc = v[0];
 #pragma unroll
         for (int s = 1; s < kMaxSplits; ++s)
-            if (s < splits) acc += v[s];
-        ((f32x4 *)out)[i] = acc;
+            if (s < j.splits) acc += v[s];
+        ((f32x4 *)j.out)[i] = acc;
     }
 }
 
@@ -272,6 +294,29 @@ void grad_split(int64_t tiles, int64_t K, int64_t &splits, int64_t &chunk) {
                                                 K / (kBK * kSplitMinSteps), (int64_t)kMaxSplits}));
     chunk = round_up(ceil_div(K, splits), kBK);
     splits = ceil_div(K, chunk);
+}
+
+// When both gradient GEMMs are split they run as one launch, sized for one round of
+// kGroupedBlocks workgroups: the fewest K steps per workgroup (at least kSplitMinSteps)
+// for which the two tile grids times their splits fit in it.  Fewer, longer splits than
+// grad_split's also mean fewer fp32 partials to write and sum.
+constexpr int64_t kGroupedBlocks = 256;
+void grouped_split(int64_t tiles_a, int64_t K_a, int64_t tiles_b, int64_t K_b, int64_t &splits_a,
+                   int64_t &chunk_a, int64_t &splits_b, int64_t &chunk_b) {
+    const int64_t steps_a = ceil_div(K_a, kBK), steps_b = ceil_div(K_b, kBK);
+    int64_t s = std::max(kSplitMinSteps, ceil_div(tiles_a * steps_a + tiles_b * steps_b, kGroupedBlocks));
+    for (;; ++s) {   // ends: at s = max(steps_a, steps_b) both split counts are 1
+        splits_a = ceil_div(steps_a, s);
+        splits_b = ceil_div(steps_b, s);
+        if (splits_a <= kMaxSplits && splits_b <= kMaxSplits &&
+            tiles_a * splits_a + tiles_b * splits_b <= kGroupedBlocks)
+            break;
+        if (splits_a == 1 && splits_b == 1) break;
+    }
+    chunk_a = s * kBK;
+    chunk_b = s * kBK;
+    splits_a = ceil_div(K_a, chunk_a);
+    splits_b = ceil_div(K_b, chunk_b);
 }
 
 }  // namespace
@@ -292,11 +337,23 @@ BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs) {
     b.off_wt = take((size_t)h * b.vs_ld * 2);
     b.off_dz = take((size_t)n * b.vs_ld * 2);
     b.off_dzt = take((size_t)vs * b.n_ld * 2);
-    grad_split(gemm_grid(h, n).blocks(), b.vs_ld, b.splits_dx, b.chunk_dx);
-    grad_split(gemm_grid(h, vs).blocks(), b.n_ld, b.splits_dw, b.chunk_dw);
-    const int64_t part = std::max(b.splits_dx > 1 ? b.splits_dx * n * h : 0,
-                                  b.splits_dw > 1 ? b.splits_dw * vs * h : 0);
-    b.off_split = take((size_t)part * 4);
+    const int64_t tiles_dx = gemm_grid(h, n).blocks(), tiles_dw = gemm_grid(h, vs).blocks();
+    grad_split(tiles_dx, b.vs_ld, b.splits_dx, b.chunk_dx);
+    grad_split(tiles_dw, b.n_ld, b.splits_dw, b.chunk_dw);
+    // grouped when both are split and their tiles fill at most half a round, so that the
+    // grouped launch still gives each GEMM several splits
+    b.grouped = b.splits_dx > 1 && b.splits_dw > 1 && 2 * (tiles_dx + tiles_dw) <= kGroupedBlocks;
+    if (b.grouped) {
+        grouped_split(tiles_dx, b.vs_ld, tiles_dw, b.n_ld, b.splits_dx, b.chunk_dx, b.splits_dw,
+                      b.chunk_dw);
+        b.off_split = take((size_t)b.splits_dx * n * h * 4);
+        b.off_split_dw = take((size_t)b.splits_dw * vs * h * 4);
+    } else {
+        const int64_t part = std::max(b.splits_dx > 1 ? b.splits_dx * n * h : 0,
+                                      b.splits_dw > 1 ? b.splits_dw * vs * h : 0);
+        b.off_split = take((size_t)part * 4);
+        b.off_split_dw = b.off_split;
+    }
     b.bytes = off;
     return b;
 }
@@ -321,36 +378,54 @@ hipError_t launch_bwd_grad_gemms(int64_t n, int64_t h, int64_t vs, float *dx, fl
     const uint16_t *wt = (const uint16_t *)(base + b.off_wt);
     const uint16_t *dz = (const uint16_t *)(base + b.off_dz);
     const uint16_t *dzt = (const uint16_t *)(base + b.off_dzt);
-    float *part = (float *)(base + b.off_split);
     // C^T [H, cols] = A [H, K] . B [cols, K]^T stored as out [cols, H]; split over K (into
     // the partials, then summed into out) when the output has too few tiles
+    const Operand ax{wt, b.vs_ld, (int)h}, bx{dz, b.vs_ld, (int)n};      // dX_r^T = W_r^T dz^T
+    const Operand aw{xt, b.n_ld, (int)h}, bw{dzt, b.n_ld, (int)vs};      // dW_r^T = X^T dz
+    auto split_job = [&](Operand A, Operand B, int64_t K, int64_t cols, int64_t splits,
+                         int64_t chunk, float *part) {
+        const GemmGrid g = gemm_grid(h, cols);
+        return SplitJob{A, B, (int)K, (int)chunk, g, StoreTransposedEpilogue{part, h, (int)h, (int)cols},
+                        cols * h, (int)(g.blocks() * splits)};
+    };
+    auto sum_job = [&](float *part, int64_t splits, int64_t cols, float *out) {
+        return SumJob{part, (int)splits, cols * h, cols * h, out};
+    };
+    auto sum_launch = [&](SumJob j0, SumJob j1) {
+        const int64_t n4 = (j0.count + j1.count) / 4;
+        hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(n4, 256), 8192)),
+                           dim3(256), 0, stream, j0, j1);
+    };
+    const SplitJob none{};
+    const SumJob no_sum{};
+    if (b.grouped) {   // both split: one launch for the two GEMMs, one for the two sums
+        float *px = (float *)(base + b.off_split), *pw = (float *)(base + b.off_split_dw);
+        const SplitJob jx = split_job(ax, bx, b.vs_ld, n, b.splits_dx, b.chunk_dx, px);
+        const SplitJob jw = split_job(aw, bw, b.n_ld, vs, b.splits_dw, b.chunk_dw, pw);
+        hipLaunchKernelGGL(gemm_nt_splitk_store_kernel, dim3((unsigned)(jx.blocks + jw.blocks)),
+                           dim3(kThreads), 0, stream, jx, jw);
+        sum_launch(sum_job(px, b.splits_dx, n, dx), sum_job(pw, b.splits_dw, vs, dw));
+        return hipGetLastError();
+    }
+    float *part = (float *)(base + b.off_split);
     auto gemm = [&](Operand A, Operand B, int64_t K, int64_t cols, int64_t splits, int64_t chunk,
                     float *out) -> hipError_t {
-        const GemmGrid g = gemm_grid(h, cols);
         if (splits == 1) {
+            const GemmGrid g = gemm_grid(h, cols);
             StoreTransposedEpilogue epi{out, h, (int)h, (int)cols};
             hipLaunchKernelGGL(gemm_nt_kernel<StoreTransposedEpilogue>, dim3(g.blocks()),
                                dim3(kThreads), 0, stream, A, B, (int)K, g.tiles_m, g.tiles_n, epi);
             return hipGetLastError();
         }
-        StoreTransposedEpilogue epi{part, h, (int)h, (int)cols};
-        hipLaunchKernelGGL(gemm_nt_splitk_store_kernel, dim3((unsigned)(g.blocks() * splits)),
-                           dim3(kThreads), 0, stream, A, B, (int)K, (int)chunk, g.tiles_m,
-                           g.tiles_n, epi, cols * h);
-        const int64_t count = cols * h;
-        hipLaunchKernelGGL(sum_splits_kernel,
-                           dim3((unsigned)std::min<int64_t>(ceil_div(count / 4, 256), 8192)),
-                           dim3(256), 0, stream, part, (int)splits, count, count, out);
+        const SplitJob j = split_job(A, B, K, cols, splits, chunk, part);
+        hipLaunchKernelGGL(gemm_nt_splitk_store_kernel, dim3((unsigned)j.blocks), dim3(kThreads), 0,
+                           stream, j, none);
+        sum_launch(sum_job(part, splits, cols, out), no_sum);
         return hipGetLastError();
     };
     hipError_t e;
-    // dX_r^T [H, N] = W_r^T [H, Vs64] . dz [N, Vs64]^T
-    if ((e = gemm(Operand{wt, b.vs_ld, (int)h}, Operand{dz, b.vs_ld, (int)n}, b.vs_ld, n,
-                  b.splits_dx, b.chunk_dx, dx)) != hipSuccess)
-        return e;
-    // dW_r^T [H, Vs] = X^T [H, N64] . dz^T [Vs, N64]^T
-    return gemm(Operand{xt, b.n_ld, (int)h}, Operand{dzt, b.n_ld, (int)vs}, b.n_ld, vs, b.splits_dw,
-                b.chunk_dw, dw);
+    if ((e = gemm(ax, bx, b.vs_ld, n, b.splits_dx, b.chunk_dx, dx)) != hipSuccess) return e;
+    return gemm(aw, bw, b.n_ld, vs, b.splits_dw, b.chunk_dw, dw);
 }
 
 hipError_t launch_bwd_zero_dw(float *dw, int64_t vs, int64_t h, hipStream_t stream) {

@@ -23,9 +23,12 @@ FwdWorkspace fwd_workspace(int64_t n, int64_t vs);
 struct BwdWorkspace {
     int64_t n_ld, vs_ld;   // padded leading dimensions (multiples of 64)
     size_t off_xt, off_wt, off_dz, off_dzt;
-    // split-K of the two gradient GEMMs (1: none) and the partials region they share
+    // split-K of the two gradient GEMMs (1: none) and their partials.  When both are split
+    // they run as one launch (grouped) and their partials sit side by side (dX's at
+    // off_split, dW's at off_split_dw); otherwise they share off_split.
     int64_t splits_dx, chunk_dx, splits_dw, chunk_dw;
-    size_t off_split;
+    bool grouped;
+    size_t off_split, off_split_dw;
     size_t bytes;
 };
 BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs);
