@@ -207,6 +207,16 @@ def test_bwd_validation_and_workspace(lib):
     n64, vs64 = r64(n), r64(vs)
     assert need == r256(h * n64 * 2) + r256(h * vs64 * 2) + r256(n * vs64 * 2) + r256(vs * n64 * 2)
     assert ws(6, 32, 0, 4) == r256(32 * 64 * 2) * 2 + r256(6 * 64 * 2) + r256(4 * 64 * 2)
+    # small LM (n 4096, h 512, Vs 3200): dX (2 x 16 tiles) and dW (2 x 13 tiles) both split
+    # over K, so they run as one launch of one round: 16 K steps per workgroup, 4 + 4 splits,
+    # 232 workgroups, with both GEMMs' fp32 partials side by side after the bf16 buffers
+    def bufs(n_, h_, vs_):   # the four bf16 buffers
+        return (r256(h_ * r64(n_) * 2) + r256(h_ * r64(vs_) * 2) + r256(n_ * r64(vs_) * 2)
+                + r256(vs_ * r64(n_) * 2))
+    assert ws(4096, 512, 0, 3200) == (bufs(4096, 512, 3200) + r256(4 * 4096 * 512 * 4)
+                                      + r256(4 * 3200 * 512 * 4))
+    # only dX split (dW's K is 64 tokens: one pass): a single partials region, 2 splits
+    assert ws(64, 520, 0, 1000) == bufs(64, 520, 1000) + r256(2 * 64 * 520 * 4)
     f = lib.vp_lmhead_ce_bwd
     base = dict(x=FAKE, w=FAKE, t=FAKE, lse=FAKE, n=n, h=h, lo=0, hi=vs, ign=-100, g=1.0,
                 dx=FAKE, dw=FAKE, ws=FAKE, wsb=need)
