@@ -274,6 +274,36 @@ def test_deterministic(vp):
             assert torch.equal(runs[0]["grads"][t][k], runs[1]["grads"][t][k]), (t, k)
 
 
+@pytest.mark.parametrize("shape", [(8192, 4096, 16032), (4096, 512, 3200)],
+                         ids=["shard_8b", "small_lm"])
+def test_deterministic_at_full_size(vp, shape):
+    """The GEMMs order their LDS traffic with explicit waits and barriers; a missing wait
+    would show as run-to-run differences under full load.  Three runs of the forward,
+    combine (T = 1) and backward on the same inputs must give the same bits: at the
+    8B-class shard (2016, 512 and 1008 tiles) and at the small LM, whose two gradient GEMMs
+    split over K in one grouped launch."""
+    import torch
+    N, H, Vs = shape
+    g = torch.Generator(device="cuda").manual_seed(N + H)
+    x = torch.randn((N, H), device="cuda", generator=g).bfloat16()
+    w = (0.02 * torch.randn((Vs, H), device="cuda", generator=g)).bfloat16()
+    y = torch.randint(0, 8 * Vs, (N,), device="cuda", generator=g)
+    y[::13] = -100
+    log(f"  N={N} H={H} Vs={Vs}: three runs")
+    runs = []
+    for _ in range(3):
+        m, s, zy = vp.vp_lmhead_ce_fwd(x, w, y, 0, Vs)
+        loss, lse, mean = vp.vp_ce_combine(m[None], s[None], zy[None], y)
+        dx, dw = vp.vp_lmhead_ce_bwd(x, w, y, lse, 0, Vs, 1.0 / N)
+        torch.cuda.synchronize()
+        runs.append((m, s, zy, loss, lse, mean, dx, dw))
+    names = ("m", "s", "zy", "loss", "lse", "mean", "dx", "dw")
+    for r in runs[1:]:
+        for name, a, b in zip(names, runs[0], r):
+            assert torch.equal(a, b), f"{name} differs between runs"
+    assert bool(torch.isfinite(runs[0][6]).all()) and bool(torch.isfinite(runs[0][7]).all())
+
+
 @pytest.mark.parametrize("scale", [1.0, 0.0, -0.25, 4096.0])
 def test_grad_scale_other_than_the_mean(vp, scale):
     """grad_scale is the caller's upstream factor: 1 for a summed loss, 0, a negative one,
