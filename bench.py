@@ -351,6 +351,47 @@ def reduce_mfma(path, cmd):
     print("\n".join(lines))
 
 
+LDS_PROFILE = os.path.join(ROOT, "profiles", "lds_counters_shard_8b.txt")
+LDS_COUNTERS = "SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_WAVE_CYCLES"
+
+
+def reduce_lds(path, cmd):
+    """Summarise one counter run of this script (LDS_COUNTERS with --kernel-trace) into
+    LDS_PROFILE: per GEMM kernel, LDS instructions per MFMA, the share of wave cycles spent
+    waiting on LDS instructions, and the LDS bank-conflict cycles per LDS instruction."""
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        k = int(r["Dispatch_Id"])
+        e = acc.setdefault(k, {"name": short_kernel_name(r["Kernel_Name"]),
+                               "grid": r.get("Grid_Size", r.get("Grid_Size_X", ""))})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    rows = {}
+    for k in sorted(acc):
+        e = acc[k]
+        if e.get("SQ_INSTS_MFMA", 0) == 0:
+            continue
+        rows.setdefault((e["name"], e["grid"]), []).append(
+            (e["SQ_INSTS_LDS"] / e["SQ_INSTS_MFMA"], e["SQ_WAIT_INST_LDS"] / e["SQ_WAVE_CYCLES"],
+             e["SQ_LDS_BANK_CONFLICT"], e["SQ_LDS_BANK_CONFLICT"] / max(1.0, e["SQ_INSTS_LDS"])))
+    lines = ["# LDS use of every GEMM kernel in one bench run (rocprofv3 counters)",
+             "# command (from the repository root):", f"#   {cmd}",
+             f"#   python3 bench.py --reduce-lds <counter csv>   (writes this file)",
+             "# lds/mfma = SQ_INSTS_LDS / SQ_INSTS_MFMA (the mainloop issues 24 ds_read_b128 per",
+             "# 64 MFMAs, 0.375; epilogues add their own); lds_wait = SQ_WAIT_INST_LDS /",
+             "# SQ_WAVE_CYCLES; bank_conflict = SQ_LDS_BANK_CONFLICT cycles, also per LDS instruction.",
+             "# The Cijk_* kernels are hipBLASLt's (torch.matmul yardsticks at the same shapes).",
+             f"kernel_source_hash: {kernel_source_hash()}", "",
+             "dispatches  lds/mfma  lds_wait  bank_conflict_cycles  per_lds_inst  kernel [grid]"]
+    for (name, grid), v in rows.items():
+        n = len(v)
+        ratio, wait, conf, per = (sum(x[i] for x in v) / n for i in range(4))
+        lines.append(f"{n:10d} {ratio:9.3f} {wait * 100:8.1f}% {conf:21.0f} {per:13.4f}  "
+                     f"{name[:70]} [{grid}]")
+    with open(LDS_PROFILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _run_text(cmd, timeout=30):
     """stdout of a command, or None if it is missing or fails (information only)."""
     import subprocess
@@ -507,6 +548,9 @@ def main():
     ap.add_argument("--reduce-mfma", metavar="COUNTER_CSV",
                     help="summarise a rocprofv3 --pmc run of this script with MFMA_COUNTERS and "
                          "--kernel-trace into profiles/ and exit (no GPU needed)")
+    ap.add_argument("--reduce-lds", metavar="COUNTER_CSV",
+                    help="summarise a rocprofv3 --pmc run of this script with LDS_COUNTERS and "
+                         "--kernel-trace into profiles/ and exit (no GPU needed)")
     ap.add_argument("--reduce-pmc-lookup", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script's lookup benches into profiles/ and exit (no GPU needed)")
@@ -529,6 +573,11 @@ def main():
         reduce_mfma(args.reduce_mfma,
                     f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv -d "
                     f"{os.path.dirname(args.reduce_mfma)} {run_args}")
+        return
+    if args.reduce_lds:
+        reduce_lds(args.reduce_lds,
+                   f"rocprofv3 --pmc {LDS_COUNTERS} --kernel-trace --output-format csv -d "
+                   f"{os.path.dirname(args.reduce_lds)} {run_args}")
         return
     if args.reduce_pmc:
         cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {os.path.dirname(path)} {run_args}"
