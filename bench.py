@@ -54,7 +54,8 @@ def log(msg):
 
 
 # the sources the CE sequence's kernels are compiled from (and the build flags)
-CE_SOURCES = ("common.hpp", "gemm.hpp", "launch.hpp", "ce_fwd.hip", "ce_combine.hip", "ce_bwd.hip")
+CE_SOURCES = ("common.hpp", "gemm.hpp", "gemm_small.hpp", "launch.hpp", "ce_fwd.hip",
+              "ce_combine.hip", "ce_bwd.hip")
 
 
 # the sources the lookup's and its gradient's kernels are compiled from

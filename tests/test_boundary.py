@@ -207,16 +207,23 @@ def test_bwd_validation_and_workspace(lib):
     n64, vs64 = r64(n), r64(vs)
     assert need == r256(h * n64 * 2) + r256(h * vs64 * 2) + r256(n * vs64 * 2) + r256(vs * n64 * 2)
     assert ws(6, 32, 0, 4) == r256(32 * 64 * 2) * 2 + r256(6 * 64 * 2) + r256(4 * 64 * 2)
-    # small LM (n 4096, h 512, Vs 3200): dX (2 x 16 tiles) and dW (2 x 13 tiles) both split
-    # over K, so they run as one launch of one round: 16 K steps per workgroup, 4 + 4 splits,
-    # 232 workgroups, with both GEMMs' fp32 partials side by side after the bf16 buffers
     def bufs(n_, h_, vs_):   # the four bf16 buffers
         return (r256(h_ * r64(n_) * 2) + r256(h_ * r64(vs_) * 2) + r256(n_ * r64(vs_) * 2)
                 + r256(vs_ * r64(n_) * 2))
-    assert ws(4096, 512, 0, 3200) == (bufs(4096, 512, 3200) + r256(4 * 4096 * 512 * 4)
-                                      + r256(4 * 3200 * 512 * 4))
-    # only dX split (dW's K is 64 tokens: one pass): a single partials region, 2 splits
-    assert ws(64, 520, 0, 1000) == bufs(64, 520, 1000) + r256(2 * 64 * 520 * 4)
+    # small LM (n 4096, h 512, Vs 3200): as 128 x 128 tiles dX has 4 x 32 and dW 4 x 25, one
+    # round of 228 workgroups, with K loops of 50 and 64 steps: one launch, no fp32 partials
+    assert ws(4096, 512, 0, 3200) == bufs(4096, 512, 3200)
+    assert ws(64, 520, 0, 1000) == bufs(64, 520, 1000)
+    # n 2048, h 512, Vs 9000: 348 small tiles, so 256 x 256 tiles (dX 2 x 8, dW 2 x 36), both
+    # split over K in one grouped launch sized for one round: 21 K steps per workgroup,
+    # 7 + 2 splits, both GEMMs' fp32 partials side by side
+    assert ws(2048, 512, 0, 9000) == (bufs(2048, 512, 9000) + r256(7 * 2048 * 512 * 4)
+                                      + r256(2 * 9000 * 512 * 4))
+    # only dX split (n 256, h 512, Vs 16000: dX K 250 steps over 2 tiles; dW's K is 4 steps):
+    # 16 splits in a single partials region
+    assert ws(256, 512, 0, 16000) == bufs(256, 512, 16000) + r256(16 * 256 * 512 * 4)
+    # only dW split (n 12000, h 64, Vs 900: dW's K is 188 steps over 4 tiles; dX's 15)
+    assert ws(12000, 64, 0, 900) == bufs(12000, 64, 900) + r256(16 * 900 * 64 * 4)
     f = lib.vp_lmhead_ce_bwd
     base = dict(x=FAKE, w=FAKE, t=FAKE, lse=FAKE, n=n, h=h, lo=0, hi=vs, ign=-100, g=1.0,
                 dx=FAKE, dw=FAKE, ws=FAKE, wsb=need)

@@ -22,6 +22,7 @@
 #include <type_traits>
 
 #include "gemm.hpp"
+#include "gemm_small.hpp"
 #include "launch.hpp"
 
 namespace vp {
@@ -319,6 +320,20 @@ void grouped_split(int64_t tiles_a, int64_t K_a, int64_t tiles_b, int64_t K_b, i
     splits_b = ceil_div(K_b, chunk_b);
 }
 
+// The 128 x 128-tile launch (no split) is taken when both products' tiles fit one round
+// of workgroups and neither K loop exceeds kSmallMaxSteps steps.  Beyond that the 256 x 256
+// tiles' higher throughput per CU outweighs the split's partials.  Measured at the small LM
+// (N 4096, H 512, Vs 3200; 128 + 100 tiles of 50 and 64 K steps): 36-38 us against 47-49 us
+// for the grouped split launch and its sum; at N = H = Vs = 2048 with H 1024: 23.5 against
+// 42 us.
+constexpr int64_t kSmallMaxBlocks = 256;
+constexpr int64_t kSmallMaxSteps = 128;
+int64_t small_tiles(int64_t M, int64_t N) { return ceil_div(M, kSBM) * ceil_div(N, kSBN); }
+bool small_path(int64_t n, int64_t h, int64_t vs) {
+    return small_tiles(h, n) + small_tiles(h, vs) <= kSmallMaxBlocks &&
+           ceil_div(vs, kBK) <= kSmallMaxSteps && ceil_div(n, kBK) <= kSmallMaxSteps;
+}
+
 }  // namespace
 
 BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs) {
@@ -337,6 +352,15 @@ BwdWorkspace bwd_workspace(int64_t n, int64_t h, int64_t vs) {
     b.off_wt = take((size_t)h * b.vs_ld * 2);
     b.off_dz = take((size_t)n * b.vs_ld * 2);
     b.off_dzt = take((size_t)vs * b.n_ld * 2);
+    if (small_path(n, h, vs)) {   // no split, no partials
+        b.splits_dx = b.splits_dw = 1;
+        b.chunk_dx = b.vs_ld;
+        b.chunk_dw = b.n_ld;
+        b.grouped = false;
+        b.off_split = b.off_split_dw = off;
+        b.bytes = off;
+        return b;
+    }
     const int64_t tiles_dx = gemm_grid(h, n).blocks(), tiles_dw = gemm_grid(h, vs).blocks();
     grad_split(tiles_dx, b.vs_ld, b.splits_dx, b.chunk_dx);
     grad_split(tiles_dw, b.n_ld, b.splits_dw, b.chunk_dw);
@@ -396,6 +420,15 @@ hipError_t launch_bwd_grad_gemms(int64_t n, int64_t h, int64_t vs, float *dx, fl
         hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(n4, 256), 8192)),
                            dim3(256), 0, stream, j0, j1);
     };
+    if (small_path(n, h, vs)) {   // both products as 128 x 128 tiles in one launch, stored directly
+        const SmallJob jx{ax, bx, (int)b.vs_ld, (int)ceil_div(h, kSBM), (int)ceil_div(n, kSBN),
+                          dx, h, (int)h, (int)n};
+        const SmallJob jw{aw, bw, (int)b.n_ld, (int)ceil_div(h, kSBM), (int)ceil_div(vs, kSBN),
+                          dw, h, (int)h, (int)vs};
+        hipLaunchKernelGGL(gemm_nt_small_kernel, dim3((unsigned)(jx.blocks() + jw.blocks())),
+                           dim3(kSThreads), 0, stream, jx, jw, jx.blocks(), jx.blocks() + jw.blocks());
+        return hipGetLastError();
+    }
     const SplitJob none{};
     const SumJob no_sum{};
     if (b.grouped) {   // both split: one launch for the two GEMMs, one for the two sums

@@ -29,7 +29,11 @@
 // (into the other stage, which group 1 finished reading in interval 2k - 1); interval
 // 2k + 1 holds group 1's reads of step k, then, once they are complete, its loads of
 // B(k+2) into the same stage (group 0 read it in interval 2k).  Each load has landed
-// before the interval of its first read begins.
+// before the interval of its first read begins.  That early B load relies on each wave of
+// group 1 reading exactly the 64 B rows it loads itself (its N columns are its slab): the
+// wave's own wait for its reads is then the only one needed before it overwrites them.
+// A layout in which one wave reads rows another wave of its group loads would need a
+// barrier there instead.
 //
 // Rows past M / N read as zeros (outside the buffer resource; the epilogue
 // masks them); K chunks past K are zero-filled, so K need only be a multiple
@@ -158,7 +162,7 @@ __device__ __forceinline__ void gemm_nt_tile(const Operand &A, const Operand &B,
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int grp = wave >> 2, slab = wave & 3;   // group; the wave's place in it (its SIMD)
-    const int wm = grp, wn = slab;
+    const int wm = grp, wn = slab;   // wn == slab: a wave reads the B rows it loads
 
     // Global -> LDS map (buffer loads straight into LDS, 16 bytes per lane).  One wave
     // instruction fills 8 rows x 128 B = 1 KiB of LDS in lane order: lane L lands on
