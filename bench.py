@@ -102,7 +102,7 @@ def recorded_traffic():
 
 CE_KERNELS = ("CeStatsEpilogue", "merge_slices_kernel", "combine_kernel", "mean_kernel",
               "transpose_bf16_kernel", "DlogitsEpilogue", "StoreTransposedEpilogue",
-              "gemm_nt_splitk_store_kernel", "sum_splits_kernel")
+              "gemm_nt_splitk_store_kernel", "sum_splits_kernel", "gemm_nt_small_kernel")
 
 
 def short_kernel_name(name: str) -> str:

@@ -36,7 +36,7 @@ def program():
 @pytest.mark.parametrize("N,H,V,T", [(300, 136, 2100, 3), (4096, 512, 6400, 2)])
 def test_step_through_the_c_abi(program, tmp_path, N, H, V, T):
     """Ragged tiles (300 x 136, three shards of 700) and the small-LM shape, whose gradient
-    GEMMs are split over K; 10% of the targets ignored."""
+    GEMMs run as 128 x 128 tiles in one launch; 10% of the targets ignored."""
     r = np.random.default_rng(N + V)
     xb = vp_inputs.f32_to_bf16_bits(r.standard_normal((N, H)).astype(np.float32))
     wb = vp_inputs.f32_to_bf16_bits(

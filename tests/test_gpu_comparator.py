@@ -151,8 +151,8 @@ def test_shard_8b_against_golden(vp):
 
 def _sweep_cases():
     """Seeded shapes: odd N (1-2500), H a multiple of 8 (8-1024), Vs 1-5000 with T 1-4,
-    so that stored rows are padded by 0-3 columns and the gradient GEMMs run single-pass
-    or split over K; alternating one-read and two-pass statistics."""
+    so that stored rows are padded by 0-3 columns and the gradient GEMMs run as 128 x 128
+    tiles or split over K; alternating one-read and two-pass statistics."""
     r = np.random.default_rng(4242)
     out = []
     for i in range(12):

@@ -281,7 +281,7 @@ def test_deterministic_at_full_size(vp, shape):
     would show as run-to-run differences under full load.  Three runs of the forward,
     combine (T = 1) and backward on the same inputs must give the same bits: at the
     8B-class shard (2016, 512 and 1008 tiles) and at the small LM, whose two gradient GEMMs
-    split over K in one grouped launch."""
+    run as 128 x 128 tiles in one launch."""
     import torch
     N, H, Vs = shape
     g = torch.Generator(device="cuda").manual_seed(N + H)

@@ -1,7 +1,8 @@
 """A seeded sweep of 24 random small shapes through the whole CE path, each compared in full
 with the oracle: odd N, H (a multiple of 8) and Vs, T = 1..5, 10% ignored targets.  The
 shapes are drawn so that the forward's slice merge runs in one pass and split 2-5 ways,
-and the gradient GEMMs run single-pass and split over K 2-16 ways, in many combinations.
+and the gradient GEMMs run as 128 x 128 tiles in one launch (18 shapes) or, for the wide
+shards, split over K (6), in many combinations.
 A second sweep of 24 random shapes covers the lookup and its gradient.
 Same bars as the other parity tests."""
 from __future__ import annotations
@@ -27,7 +28,7 @@ def _cases():
         if i % 4 == 0:     # few tokens, a wide shard: the merge splits, dX splits over K
             N, H, Vs = int(r.integers(1, 200)), 8 * int(r.integers(1, 17)), int(r.integers(8000, 24000))
             T = min(T, 2)
-        elif i % 4 == 1:   # many tokens, a narrow shard: dW splits over K
+        elif i % 4 == 1:   # many tokens, a narrow shard
             N, H, Vs = int(r.integers(1000, 3000)), 8 * int(r.integers(1, 65)), int(r.integers(1, 1500))
         elif i % 4 == 2:
             N, H, Vs = int(r.integers(1, 700)), 8 * int(r.integers(1, 129)), int(r.integers(1, 3000))
