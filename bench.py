@@ -108,7 +108,8 @@ CE_KERNELS = ("CeStatsEpilogue", "merge_slices_kernel", "combine_kernel", "mean_
 def short_kernel_name(name: str) -> str:
     """A kernel's short name in profiler output: the epilogue of a GEMM instance
     (gemm_nt_kernel<...Epilogue>), otherwise the function's own name."""
-    m = re.search(r"gemm_nt_kernel<(?:[\w:]*::)?(?:\(anonymous namespace\)::)?(\w+)>", name)
+    m = re.search(r"gemm_nt_kernel<(?:[\w:]*::)?(?:\(anonymous namespace\)::)?(\w+)(?:<[^<>]*>)?\s*>",
+                  name)
     if m:
         return m.group(1)
     m = re.search(r"(\w+)(?:<[^<>()]*>)?\(", name)

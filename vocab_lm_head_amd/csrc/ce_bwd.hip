@@ -101,6 +101,10 @@ __device__ __forceinline__ int dz_swz(int row, int col) {
     return row * kBM + ((((col >> 3) ^ ((row ^ (row >> 3)) & 31)) << 3) | (col & 7));
 }
 
+// kPolicy: the cache policy of the dz stores (kStoreNT where dz and dz^T outsize the caches
+// and would evict the panels the GEMMs still read; the default where they fit, so that
+// the gradient GEMMs read them back from the caches).
+template <int kPolicy>
 struct DlogitsEpilogue {
     const int64_t *targets;
     const float *lse;
@@ -179,7 +183,7 @@ struct DlogitsEpilogue {
                 v[it] = *(const u32x4 *)(lds + dz_swz(r0 + kRowStep * it, 8 * c));
 #pragma unroll
             for (int it = 0; it < kIt; ++it)
-                store16<kStoreNT>(v[it], rs,
+                store16<kPolicy>(v[it], rs,
                         colok ? (uint32_t)(((int64_t)(r0 + kRowStep * it) * ld_dz + 8 * c) * 2) : kOutOfRange);
         }
         {   // vocab-major: a lane gathers 4 vocab rows x 8 tokens (eight 8-byte LDS reads)
@@ -207,7 +211,7 @@ struct DlogitsEpilogue {
                         o[p] = ((rd[it][2 * p][w] >> sh) & 0xFFFFu) |
                                (((rd[it][2 * p + 1][w] >> sh) & 0xFFFFu) << 16);
                     const int64_t row = vq + kVocabStep * it + v;
-                    store16<kStoreNT>(o, rs, colok ? (uint32_t)((row * ld_dzt + c) * 2) : kOutOfRange);
+                    store16<kPolicy>(o, rs, colok ? (uint32_t)((row * ld_dzt + c) * 2) : kOutOfRange);
                 }
         }
     }
@@ -281,6 +285,10 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(SumJob j0, SumJob j1) {
         ((f32x4 *)j.out)[i] = acc;
     }
 }
+
+// dz and dz^T together up to this size are stored with the default cache policy (they stay
+// in the 256 MB Infinity Cache for the gradient GEMMs); larger ones non-temporally.
+constexpr int64_t kDzCachedBytes = (int64_t)64 << 20;
 
 // K splits of a gradient GEMM with `tiles` output tiles: below one tile per CU the K
 // loop is split (aiming at kSplitTargetBlocks workgroups, at least kSplitMinSteps K
@@ -481,11 +489,17 @@ hipError_t launch_ce_bwd(const uint16_t *x, const uint16_t *w, const int64_t *ta
     if ((e = launch_bwd_transposes(x, w, n, h, vs, ws, stream)) != hipSuccess) return e;
     {   // recompute + dlogits: rows = vocab (A = W_r), cols = tokens (B = X)
         const GemmGrid g = gemm_grid(vs, n);
-        DlogitsEpilogue epi{targets, lse, start, ignore_index, grad_scale, (int)vs, (int)n,
-                            b.vs_ld, b.n_ld, dz, dzt};
-        hipLaunchKernelGGL(gemm_nt_kernel<DlogitsEpilogue>, dim3(g.blocks()), dim3(kThreads), 0,
-                           stream, Operand{w, h, (int)vs}, Operand{x, h, (int)n}, (int)h,
-                           g.tiles_m, g.tiles_n, epi);
+        const Operand a{w, h, (int)vs}, bx{x, h, (int)n};
+        auto launch = [&](auto epi) {
+            hipLaunchKernelGGL(gemm_nt_kernel<decltype(epi)>, dim3(g.blocks()), dim3(kThreads), 0,
+                               stream, a, bx, (int)h, g.tiles_m, g.tiles_n, epi);
+        };
+        if ((int64_t)(b.off_dzt - b.off_dz) * 2 <= kDzCachedBytes)
+            launch(DlogitsEpilogue<kStoreDefault>{targets, lse, start, ignore_index, grad_scale,
+                                                  (int)vs, (int)n, b.vs_ld, b.n_ld, dz, dzt});
+        else
+            launch(DlogitsEpilogue<kStoreNT>{targets, lse, start, ignore_index, grad_scale,
+                                             (int)vs, (int)n, b.vs_ld, b.n_ld, dz, dzt});
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_bwd_grad_gemms(n, h, vs, dx, dw, ws, stream);
