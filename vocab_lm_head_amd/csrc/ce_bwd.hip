@@ -15,6 +15,10 @@
 //      writes it in bf16 twice, token-major dz [N, Vs64] and vocab-major dz^T [Vs, N64];
 //   3. dX_r^T = W_r^T dz^T  (A = W_r^T [H, Vs64], B = dz [N, Vs64]), K = Vs64
 //   4. dW_r^T = X^T dz      (A = X^T [H, N64],   B = dz^T [Vs, N64]),  K = N64
+//      Steps 3 and 4 run as one launch of 128 x 128 tiles when both fit one round of
+//      workgroups with short K loops (gemm_small.hpp); otherwise as 256 x 256 tiles,
+//      split over K into fp32 partials (then summed in split order) when an output has
+//      fewer tiles than CUs.
 // The [N, Vs] dlogits must reach memory once: a register-only fusion of dX and
 // dW would need fp32 atomics on [tile, H] slabs for every tile, far below the
 // MFMA roofline at H = 4096.
