@@ -79,41 +79,45 @@ __global__ __launch_bounds__(kSortThreads) void radix_count_kernel(KeySource src
     if (t < kRadix) hist[(int64_t)t * nblk + blockIdx.x] = cnt[t];
 }
 
-// In-place exclusive scan of `count` values by one workgroup: thread t scans its
-// contiguous chunk (read and rewritten 16 bytes at a time, kScanBatch loads in
-// flight), the chunk sums are scanned in LDS.  count is a multiple of 4 (kRadix x
-// tiles) and hist is 16-byte aligned.
+// In-place exclusive scan of `count` values by one workgroup: thread t takes a contiguous
+// chunk (16-byte loads, kScanBatch in flight), the chunk sums are scanned across the
+// workgroup (within each wave by shuffles, then over the waves' totals in LDS, one
+// barrier), and each thread rewrites its chunk.  Chunks of up to kScanBatch x 4 values
+// stay in registers between the two; longer ones are read again.  count is a multiple
+// of 4 (kRadix x tiles) and hist is 16-byte aligned.
 constexpr int kScanBatch = 8;
 __global__ __launch_bounds__(kScanThreads) void radix_scan_kernel(uint32_t *hist, int64_t count) {
-    __shared__ uint32_t part[2][kScanThreads];
-    const int t = threadIdx.x;
+    __shared__ uint32_t wave_total[kScanThreads / 64];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t chunk = round_up(ceil_div(count, kScanThreads), 4);
     const int64_t a = min(t * chunk, count), b = min(a + chunk, count);
+    const bool in_regs = chunk <= 4 * kScanBatch;   // uniform
     u32x4 *h4 = (u32x4 *)hist;
+    u32x4 v[kScanBatch];
     uint32_t sum = 0;
-    for (int64_t i = a; i < b; i += 4 * kScanBatch) {
-        u32x4 v[kScanBatch];
+    for (int64_t i = a; i < b; i += 4 * kScanBatch) {   // one trip when in_regs
 #pragma unroll
         for (int u = 0; u < kScanBatch; ++u)
             v[u] = i + 4 * u < b ? h4[(i >> 2) + u] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < kScanBatch; ++u) sum += v[u][0] + v[u][1] + v[u][2] + v[u][3];
     }
-    part[0][t] = sum;
-    __syncthreads();
-    int cur = 0;
-    for (int off = 1; off < kScanThreads; off <<= 1) {   // inclusive Hillis-Steele scan
-        const uint32_t v = part[cur][t] + (t >= off ? part[cur][t - off] : 0u);
-        part[cur ^ 1][t] = v;
-        cur ^= 1;
-        __syncthreads();
-    }
-    uint32_t run = part[cur][t] - sum;   // exclusive prefix of this chunk
-    for (int64_t i = a; i < b; i += 4 * kScanBatch) {
-        u32x4 v[kScanBatch];
+    uint32_t incl = sum;   // inclusive scan of the chunk sums within the wave
 #pragma unroll
-        for (int u = 0; u < kScanBatch; ++u)
-            v[u] = i + 4 * u < b ? h4[(i >> 2) + u] : u32x4{0u, 0u, 0u, 0u};
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t up = __shfl_up(incl, o);
+        if (lane >= o) incl += up;
+    }
+    if (lane == 63) wave_total[wave] = incl;
+    __syncthreads();
+    uint32_t run = incl - sum;   // exclusive prefix of this chunk
+    for (int w = 0; w < wave; ++w) run += wave_total[w];
+    for (int64_t i = a; i < b; i += 4 * kScanBatch) {
+        if (!in_regs) {
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u)
+                v[u] = i + 4 * u < b ? h4[(i >> 2) + u] : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
         for (int u = 0; u < kScanBatch; ++u) {
             u32x4 o;
