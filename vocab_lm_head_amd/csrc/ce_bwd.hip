@@ -498,6 +498,7 @@ hipError_t launch_ce_bwd(const uint16_t *x, const uint16_t *w, const int64_t *ta
             hipLaunchKernelGGL(gemm_nt_kernel<decltype(epi)>, dim3(g.blocks()), dim3(kThreads), 0,
                                stream, a, bx, (int)h, g.tiles_m, g.tiles_n, epi);
         };
+        // dz and dz^T together: twice dz's region (dz^T's matches it up to row padding)
         if ((int64_t)(b.off_dzt - b.off_dz) * 2 <= kDzCachedBytes)
             launch(DlogitsEpilogue<kStoreDefault>{targets, lse, start, ignore_index, grad_scale,
                                                   (int)vs, (int)n, b.vs_ld, b.n_ld, dz, dzt});
